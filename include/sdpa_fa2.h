@@ -1,0 +1,125 @@
+/*
+ * sdpa_fa2.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product attention library.
+ *
+ * The library computes O = softmax(scale * Q Kᵀ + causal mask) V and the per-row logsumexp,
+ * the naive five-step attention of "PyTorch 어텐션 프로파일링 Flash, cuDNN, Math 백엔드 완벽 비교"
+ * (section 1: matmul, scale, masked_fill(-inf), softmax, matmul), without ever writing the
+ * [seq, seq] score matrix to memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory:  every tensor pointer is a DEVICE pointer (HIP device memory, or memory the device can
+ *          address).  The caller allocates and frees every buffer, including the decode
+ *          workspace; the library never allocates, frees or synchronises, and keeps no state
+ *          beyond its loaded code objects.
+ * Layout:  contiguous row-major tensors in the native [batch, heads, seq, head_dim] order
+ *          ("BNSH"), head_dim fastest:  q, out: [B, Hq, Nq, d];  k, v: [B, Hkv, Nk, d];
+ *          lse: [B, Hq, Nq] float32.  No transposes are taken or required.
+ * GQA:     Hq must be a multiple of Hkv; query head hq reads K/V head hq / (Hq / Hkv)
+ *          (K/V heads broadcast to groups of query heads, as in the FlashAttention-2 notes'
+ *          grouped-query example, "FlashAttention-2: Faster Attention with Better Parallelism
+ *          and Work Partitioning", code example).
+ * Scale:   scores are multiplied by `scale` before masking; scale == 0 selects 1/sqrt(d) (the
+ *          default of the WebGPU decode program, "[onnxruntime] WebGPU FlashAttention 최적화",
+ *          section 2).  A negative or non-finite scale is rejected.
+ * Causal:  when `causal` is non-zero, key j is visible to query i iff j <= i + (Nk - Nq), i.e. the
+ *          mask is aligned to the end of the keys; with Nq == Nk it is the usual lower triangle.
+ *          A query row with no visible key gets out = 0 and lse = -inf.
+ * LSE:     lse[b,h,i] = ln sum_j exp(scale * q_i . k_j) over visible j (natural log), float32.
+ *          `lse` may be NULL, in which case it is not written.
+ * Shapes:  every dimension must be >= 0; d must be 64 or 128.  An empty problem (B*Hq*Nq == 0)
+ *          returns ATTN_OK without launching anything.  Nk == 0 is allowed (all rows empty).
+ * Pointers: q/out must be non-NULL when B*Hq*Nq > 0, k/v when additionally Nk > 0; q, k, v, out
+ *          and the workspace must be 16-byte aligned, lse 4-byte aligned.
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work
+ *          on that stream and returns; outputs are valid once the stream reaches that point.
+ * Errors:  every check runs before anything is enqueued; on error nothing is written and a
+ *          negative ATTN_ERR_* code is returned.  ATTN_ERR_LAUNCH reports a HIP launch failure.
+ *          Kernels have no other failure mode; NaN/Inf inputs propagate into the outputs.
+ */
+#ifndef SDPA_FA2_H
+#define SDPA_FA2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,     /* a negative dimension, or a size that overflows */
+  ATTN_ERR_HEADDIM = -3,   /* d is not 64 or 128 */
+  ATTN_ERR_GQA = -4,       /* Hkv < 1 while Hq > 0, or Hq % Hkv != 0 */
+  ATTN_ERR_ALIGN = -5,     /* a tensor base address is not suitably aligned */
+  ATTN_ERR_SCALE = -6,     /* scale is negative, NaN or infinite */
+  ATTN_ERR_SPLITS = -7,    /* n_splits < 1 or n_splits > max(Nk, 1) */
+  ATTN_ERR_WORKSPACE = -8, /* workspace NULL or smaller than attn_decode_workspace_bytes() */
+  ATTN_ERR_LAUNCH = -9     /* the HIP runtime rejected a kernel launch */
+};
+
+/*
+ * attn_fwd -- fused attention forward (prefill), bfloat16 in and out, fp32 accumulation.
+ *
+ * Implements the FlashAttention-2 forward of "FlashAttention-2: Faster Attention with Better
+ * Parallelism and Work Partitioning" (section "방법론 / 알고리즘 개요": Q block outer loop, K/V
+ * block inner loop, running max and sum, one final 1/l; section "인과적 마스킹 최적화": blocks
+ * above the diagonal skipped; section "개선 2": parallel over batch x heads x Q blocks).
+ *
+ *   q   [B, Hq, Nq, d]  bf16 (read)        k, v [B, Hkv, Nk, d] bf16 (read)
+ *   out [B, Hq, Nq, d]  bf16 (written, round-to-nearest-even from fp32)
+ *   lse [B, Hq, Nq]     fp32 (written unless NULL)
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d,
+             float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_f32 -- the same operation with float32 q, k, v and out (fp32 arithmetic throughout).
+ * Same arguments, layouts and errors as attn_fwd; the tensors hold float32 instead of bf16.
+ */
+int attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, void* stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_splitkv needs:
+ *   B*Hq*Nq*n_splits*(d + 2)*4.  Returns 0 for invalid (negative) arguments.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Nq, int d, int n_splits);
+
+/*
+ * attn_decode_splitkv -- split-KV attention for few query rows against a long K/V.
+ *
+ * Two launches on `stream`, following the fused decode program and its reduce step of
+ * "[onnxruntime] WebGPU FlashAttention 최적화: 커널 퓨전과 가변 시퀀스 길이 지원으로 성능 극대화"
+ * (section 1, kernel fusion; section 2, several query rows per workgroup):
+ *   1. split kernel: for each (batch, KV head, split) the keys [s*L, min((s+1)*L, Nk)),
+ *      L = ceil(Nk / n_splits), are read once for all Hq/Hkv * Nq query rows of that KV head;
+ *      each row gets a locally normalised partial output O_s plus metadata (m_s, l_s):
+ *      m_s = max of the scaled visible scores in the split, l_s = sum exp(score - m_s).
+ *   2. combine kernel: M = max_s m_s, w_s = l_s exp(m_s - M), out = sum_s w_s O_s / sum_s w_s,
+ *      lse = M + ln sum_s w_s.
+ * Same q/k/v/out/lse conventions as attn_fwd (bf16 tensors).  The causal mask is aligned to the
+ * end of the keys (the usual decode case: the Nq new tokens are the last Nq positions).
+ *
+ * workspace: device memory of at least attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits)
+ *   bytes, owned by the caller, fully overwritten by each call:
+ *     ws_O  float32 [B, Hq, Nq, n_splits, d]   (locally normalised partial outputs)
+ *     ws_ml float32 [B, Hq, Nq, n_splits, 2]   ((m_s, l_s); empty split: (-inf, 0))
+ *   stored back to back, ws_O first.  Calls that share a workspace must be stream ordered.
+ */
+int attn_decode_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                        float scale, int causal, int n_splits, void* stream);
+
+/* attn_status_string -- a static, NUL-terminated description of a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_FA2_H */

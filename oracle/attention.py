@@ -1,0 +1,253 @@
+"""Plain fp64 CPU attention: the definition the fused kernels must reproduce.
+
+Test infrastructure only (see the package docstring): never imported by the product path.
+
+Sources (page title, then section):
+
+* "PyTorch 어텐션 프로파일링 Flash, cuDNN, Math 백엔드 완벽 비교", section 1 (naive attention): scores =
+  q·kᵀ, times scale, causal positions filled with -inf, row softmax, times v.
+* "FlashAttention-2: Faster Attention with Better Parallelism and Work Partitioning", section
+  "방법론 / 알고리즘 개요" (the forward recurrence over K/V blocks with running max m, running sum l,
+  deferred 1/l) and "인과적 마스킹 최적화" (blocks above the diagonal skipped), plus the code example's
+  ``standard_attention`` (divide by √d, ``tril`` mask) and ``fa2_with_gqa`` (K/V heads broadcast).
+* "[onnxruntime] WebGPU FlashAttention 최적화: 커널 퓨전과 가변 시퀀스 길이 지원으로 성능 극대화", section
+  "1. 커널 퓨전" (each split emits a locally normalised partial output plus (local max, local sum);
+  the reduce step rescales partials into the exact softmax-weighted V), and section "2." (the
+  default scale is 1/√head_size when the given scale is 0).
+
+Readings where the pages are silent (each applied identically everywhere):
+
+* Causal visibility is bottom-right aligned: key j is visible to query i iff j <= i + (Nk - Nq).
+  It is the square ``tril`` mask when Nq == Nk.
+* A row with no visible key has output 0 and logsumexp -inf; a split with no visible key has
+  m = -inf, l = 0, partial 0 and contributes nothing to the combine.
+* Logsumexp is the natural log of the sum of exp over the scaled, masked scores of a row.
+* GQA: query head hq reads K/V head hq // (Hq / Hkv).
+* Splits are contiguous key chunks of ceil(Nk / n_splits) keys; the last ones may be short/empty.
+
+All arithmetic is numpy float64; the matrix product (``@``) is the only library primitive.
+"""
+from __future__ import annotations
+
+import math
+from typing import Tuple
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _check(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if v.shape != k.shape or Bk != B or dk != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def visible_mask(rows: np.ndarray, Nq: int, Nk: int, causal: bool) -> np.ndarray:
+    """[len(rows), Nk] boolean: True where key j may be attended by query row i."""
+    cols = np.arange(Nk)
+    if not causal:
+        return np.ones((len(rows), Nk), dtype=bool)
+    return cols[None, :] <= (rows[:, None] + (Nk - Nq))
+
+
+def _scores(qrows: np.ndarray, kh: np.ndarray, scale: float) -> np.ndarray:
+    """Step 1-2 of the naive definition: q·kᵀ, then multiply by the scale."""
+    return (qrows @ kh.T) * scale
+
+
+def _masked_softmax(s: np.ndarray, vis: np.ndarray):
+    """Steps 3-4: fill invisible scores with -inf, then row softmax.
+
+    Returns (P, m, l) with m the row max over visible scores and l = sum exp(s - m); rows with no
+    visible key get P = 0, m = -inf, l = 0.
+    """
+    s = np.where(vis, s, NEG_INF)
+    any_vis = vis.any(axis=1)
+    m = np.where(any_vis, s.max(axis=1, initial=NEG_INF), NEG_INF)
+    shifted = np.where(vis, s - np.where(any_vis, m, 0.0)[:, None], NEG_INF)
+    e = np.exp(shifted)  # exp(-inf) = 0 for invisible entries
+    l = e.sum(axis=1)
+    p = np.divide(e, l[:, None], out=np.zeros_like(e), where=(l[:, None] > 0))
+    return p, m, l
+
+
+def _weighted_values(p: np.ndarray, vh: np.ndarray) -> np.ndarray:
+    """Step 5: probabilities times V."""
+    return p @ vh
+
+
+def _kv_head(hq: int, Hq: int, Hkv: int) -> int:
+    """GQA: contiguous groups of Hq / Hkv query heads share one K/V head."""
+    return hq // (Hq // Hkv)
+
+
+def _row_lse(m: np.ndarray, l: np.ndarray) -> np.ndarray:
+    """ln Σ exp(score) = m + ln l; -inf for rows with no visible key."""
+    ok = l > 0
+    return np.where(ok, m + np.log(np.where(ok, l, 1.0)), NEG_INF)
+
+
+def _resolve_scale(scale: float, d: int) -> float:
+    return 1.0 / math.sqrt(d) if scale == 0 else float(scale)
+
+
+def attention_fp64(q, k, v, scale: float, causal: bool, row_block: int = 1024
+                   ) -> Tuple[np.ndarray, np.ndarray]:
+    """O [B,Hq,Nq,d] and LSE [B,Hq,Nq] of softmax(scale·q·kᵀ + causal mask)·v, in fp64.
+
+    ``scale`` is the float the GPU receives (0 selects 1/√d); it is widened to fp64 unchanged.
+    Rows are processed ``row_block`` at a time only to bound memory; rows are independent.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
+    scale = _resolve_scale(scale, d)
+    out = np.zeros((B, Hq, Nq, d), dtype=np.float64)
+    lse = np.full((B, Hq, Nq), NEG_INF, dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            hkv = _kv_head(hq, Hq, Hkv)
+            for i0 in range(0, Nq, row_block):
+                rows = np.arange(i0, min(Nq, i0 + row_block))
+                s = _scores(q[b, hq, rows], k[b, hkv], scale)
+                vis = visible_mask(rows, Nq, Nk, causal)
+                p, m, l = _masked_softmax(s, vis)
+                out[b, hq, rows] = _weighted_values(p, v[b, hkv])
+                lse[b, hq, rows] = _row_lse(m, l)
+    return out, lse
+
+
+def attention_probs_fp64(q, k, scale: float, causal: bool) -> np.ndarray:
+    """The probability matrix P [B,Hq,Nq,Nk] of the definition (small inputs only)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nk, d = _check(q, k, k)
+    scale = _resolve_scale(scale, d)
+    P = np.zeros((B, Hq, Nq, Nk))
+    rows = np.arange(Nq)
+    vis = visible_mask(rows, Nq, Nk, causal)
+    for b in range(B):
+        for hq in range(Hq):
+            P[b, hq] = _masked_softmax(_scores(q[b, hq], k[b, _kv_head(hq, Hq, Hkv)], scale),
+                                       vis)[0]
+    return P
+
+
+def split_bounds(Nk: int, n_splits: int):
+    """[(start, end)] of the contiguous key chunks; chunk length ceil(Nk / n_splits)."""
+    if n_splits < 1:
+        raise ValueError("n_splits must be >= 1")
+    L = -(-Nk // n_splits)
+    return [(min(s * L, Nk), min((s + 1) * L, Nk)) for s in range(n_splits)]
+
+
+def splitkv_partials_fp64(q, k, v, scale: float, causal: bool, n_splits: int):
+    """Per-split partials of the decode model.
+
+    Returns (O_s [B,Hq,Nq,S,d], m_s [B,Hq,Nq,S], l_s [B,Hq,Nq,S]): for split s and row i,
+    m_s is the max scaled visible score in the chunk, l_s = Σ exp(score - m_s) over the chunk, and
+    O_s = Σ exp(score - m_s)·v / l_s (locally normalised).  Empty or fully masked chunks give
+    m_s = -inf, l_s = 0, O_s = 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
+    scale = _resolve_scale(scale, d)
+    bounds = split_bounds(Nk, n_splits)
+    S = len(bounds)
+    O_s = np.zeros((B, Hq, Nq, S, d))
+    m_s = np.full((B, Hq, Nq, S), NEG_INF)
+    l_s = np.zeros((B, Hq, Nq, S))
+    rows = np.arange(Nq)
+    vis_all = visible_mask(rows, Nq, Nk, causal)
+    for b in range(B):
+        for hq in range(Hq):
+            hkv = _kv_head(hq, Hq, Hkv)
+            for si, (k0, k1) in enumerate(bounds):
+                if k1 <= k0:
+                    continue
+                s = _scores(q[b, hq], k[b, hkv, k0:k1], scale)
+                p, m, l = _masked_softmax(s, vis_all[:, k0:k1])
+                O_s[b, hq, :, si] = _weighted_values(p, v[b, hkv, k0:k1])
+                m_s[b, hq, :, si] = m
+                l_s[b, hq, :, si] = l
+    return O_s, m_s, l_s
+
+
+def combine_fp64(O_s, m_s, l_s):
+    """Reduce split partials: M = max m_s, w_s = l_s·exp(m_s - M), O = Σ w_s·O_s / Σ w_s,
+    LSE = M + ln Σ w_s.  Rows whose splits are all empty give O = 0, LSE = -inf."""
+    O_s = np.asarray(O_s, dtype=np.float64)
+    m_s = np.asarray(m_s, dtype=np.float64)
+    l_s = np.asarray(l_s, dtype=np.float64)
+    M = m_s.max(axis=-1)
+    finite = np.isfinite(M)
+    Msafe = np.where(finite, M, 0.0)
+    with np.errstate(invalid="ignore"):
+        w = np.where(l_s > 0, l_s * np.exp(m_s - Msafe[..., None]), 0.0)
+    W = w.sum(axis=-1)
+    num = (w[..., None] * O_s).sum(axis=-2)
+    O = np.divide(num, W[..., None], out=np.zeros_like(num), where=(W[..., None] > 0))
+    return O, _row_lse(Msafe, W)
+
+
+def _online_step(m, l, O, S, vblk):
+    """One K/V block of the FA2 recurrence: m_new = max(m, rowmax S), P = exp(S - m_new),
+    l = exp(m - m_new)·l + rowsum P, O = exp(m - m_new)·O + P·v.  Rows whose max is still -inf
+    (nothing visible yet) keep P = 0, l = 0, O = 0."""
+    m_new = np.maximum(m, S.max(axis=1))
+    ref = np.where(np.isfinite(m_new), m_new, 0.0)
+    P = np.exp(S - ref[:, None])
+    alpha = np.exp(m - ref)
+    return m_new, alpha * l + P.sum(axis=1), alpha[:, None] * O + P @ vblk
+
+
+def flash2_tiled_fp64(q, k, v, scale: float, causal: bool, Br: int, Bc: int,
+                      skip_masked_blocks: bool = True):
+    """The FA2 forward recurrence in fp64, over Q blocks of Br rows and K/V blocks of Bc keys.
+
+    For each Q block: O = 0, l = 0, m = -inf; for each K/V block: S = scale·q·kᵀ (masked),
+    m_new = max(m, rowmax S), P = exp(S - m_new), l = exp(m - m_new)·l + rowsum P,
+    O = exp(m - m_new)·O + P·v, m = m_new; finally O / l.  With ``skip_masked_blocks`` the blocks
+    lying entirely above the causal diagonal are not visited.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
+    scale = _resolve_scale(scale, d)
+    out = np.zeros((B, Hq, Nq, d))
+    lse = np.full((B, Hq, Nq), NEG_INF)
+    off = Nk - Nq
+    for b in range(B):
+        for hq in range(Hq):
+            hkv = _kv_head(hq, Hq, Hkv)
+            for i0 in range(0, Nq, Br):
+                i1 = min(Nq, i0 + Br)
+                rows = np.arange(i0, i1)
+                qi = q[b, hq, i0:i1]
+                O = np.zeros((i1 - i0, d))
+                l = np.zeros(i1 - i0)
+                m = np.full(i1 - i0, NEG_INF)
+                for j0 in range(0, Nk, Bc):
+                    j1 = min(Nk, j0 + Bc)
+                    if causal and skip_masked_blocks and j0 > (i1 - 1) + off:
+                        break  # every later block is above the diagonal too
+                    S = (qi @ k[b, hkv, j0:j1].T) * scale
+                    vis = visible_mask(rows, Nq, Nk, causal)[:, j0:j1]
+                    S = np.where(vis, S, NEG_INF)
+                    m, l, O = _online_step(m, l, O, S, v[b, hkv, j0:j1])
+                ok = l > 0
+                out[b, hq, i0:i1] = np.divide(O, l[:, None], out=np.zeros_like(O),
+                                              where=ok[:, None])
+                lse[b, hq, i0:i1] = _row_lse(m, l)
+    return out, lse

@@ -1,0 +1,324 @@
+"""Pins of the CPU oracle to facts other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a closed form, an
+invariant of softmax attention, a library routine (scipy), brute force, or the hand-derived
+fixture under ``tests/golden/``.  ``test_oracle.py`` runs every pin; ``test_oracle_mutants.py``
+plants plausible mistakes in the oracle's steps and checks that some pin fails for each.
+
+All expected values here come from the mathematics, never from the oracle under test.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+
+from oracle import attention as A
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _tril_visible(Nq, Nk, causal):
+    """Independent construction of the end-aligned causal mask through numpy's tril."""
+    if not causal:
+        return np.ones((Nq, Nk), dtype=bool)
+    return np.tril(np.ones((Nq, Nk), dtype=bool), k=Nk - Nq)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    same_inf = (np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b)))
+    with np.errstate(invalid="ignore"):
+        err = np.where(same_inf, 0.0, np.abs(a - b))
+    assert np.all(np.isfinite(err)) and err.max(initial=0.0) <= tol, \
+        f"{what}: max err {err.max(initial=0.0)} > {tol}"
+
+
+# ---- closed forms and invariants ----------------------------------------------------------
+
+def pin_probs_rows_sum_to_one():
+    for causal in (False, True):
+        for Nq, Nk in ((7, 7), (3, 11), (11, 11), (5, 2)):
+            q = _rand(1, 1, 4, Nq, 8)
+            k = _rand(2, 1, 2, Nk, 8)
+            P = A.attention_probs_fp64(q, k, 0.3, causal)
+            vis = _tril_visible(Nq, Nk, causal)
+            has = vis.any(axis=1)
+            sums = P.sum(axis=-1)
+            _close(sums[..., has], np.ones_like(sums[..., has]), 1e-14, "row sums")
+            _close(sums[..., ~has], np.zeros_like(sums[..., ~has]), 0.0, "empty-row sums")
+            assert np.all(P[..., ~vis] == 0.0), "probability on a masked position"
+            assert np.all(P[..., vis] > 0.0), "zero probability on a visible position"
+
+
+def pin_constant_values():
+    for causal in (False, True):
+        for Nq, Nk in ((9, 9), (4, 13)):
+            q = _rand(3, 2, 4, Nq, 8)
+            k = _rand(4, 2, 2, Nk, 8)
+            c = _rand(5, 8)
+            v = np.broadcast_to(c, (2, 2, Nk, 8)).copy()
+            O, _ = A.attention_fp64(q, k, v, 0.5, causal)
+            _close(O, np.broadcast_to(c, O.shape), 1e-14, "constant V")
+
+
+def pin_identical_keys_prefix_mean():
+    for causal in (False, True):
+        for Nq, Nk in ((12, 12), (5, 12)):
+            d = 8
+            q = _rand(6, 1, 3, Nq, d)
+            kappa = _rand(7, d)
+            k = np.broadcast_to(kappa, (1, 3, Nk, d)).copy()
+            v = _rand(8, 1, 3, Nk, d)
+            scale = 0.7
+            O, lse = A.attention_fp64(q, k, v, scale, causal)
+            for h in range(3):
+                for i in range(Nq):
+                    n = min(Nk, i + (Nk - Nq) + 1) if causal else Nk
+                    _close(O[0, h, i], v[0, h, :n].mean(axis=0), 1e-14, "prefix mean")
+                    expect = scale * float(q[0, h, i] @ kappa) + math.log(n)
+                    _close(lse[0, h, i], expect, 1e-13, "prefix lse")
+
+
+def pin_causal_row_zero():
+    N, d = 10, 16
+    q = _rand(9, 2, 2, N, d)
+    k = _rand(10, 2, 2, N, d)
+    v = _rand(11, 2, 2, N, d)
+    O, lse = A.attention_fp64(q, k, v, 0.25, True)
+    _close(O[:, :, 0], v[:, :, 0], 0.0, "causal row 0 equals v_0")
+    _close(lse[:, :, 0], 0.25 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]), 1e-15,
+           "causal row 0 lse")
+
+
+def pin_gqa_equals_repeated_heads():
+    q = _rand(12, 2, 8, 6, 8)
+    k = _rand(13, 2, 2, 9, 8)
+    v = _rand(14, 2, 2, 9, 8)
+    for causal in (False, True):
+        O, lse = A.attention_fp64(q, k, v, 0.4, causal)
+        O2, lse2 = A.attention_fp64(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), 0.4,
+                                    causal)
+        _close(O, O2, 0.0, "GQA vs repeated heads")
+        _close(lse, lse2, 0.0, "GQA lse vs repeated heads")
+
+
+def pin_key_shift_invariance():
+    q = _rand(15, 1, 2, 7, 8)
+    k = _rand(16, 1, 2, 7, 8)
+    v = _rand(17, 1, 2, 7, 8)
+    u = _rand(18, 8)
+    for causal in (False, True):
+        O, lse = A.attention_fp64(q, k, v, 0.6, causal)
+        O2, lse2 = A.attention_fp64(q, k + u, v, 0.6, causal)
+        _close(O2, O, 1e-13, "key shift: O")
+        _close(lse2, lse + 0.6 * (q @ u), 1e-13, "key shift: lse")
+
+
+def pin_permutation_invariance():
+    q = _rand(19, 1, 2, 6, 8)
+    k = _rand(20, 1, 2, 11, 8)
+    v = _rand(21, 1, 2, 11, 8)
+    perm = np.random.default_rng(22).permutation(11)
+    O, lse = A.attention_fp64(q, k, v, 0.5, False)
+    O2, lse2 = A.attention_fp64(q, k[:, :, perm], v[:, :, perm], 0.5, False)
+    _close(O2, O, 1e-14, "permutation: O")
+    _close(lse2, lse, 1e-14, "permutation: lse")
+
+
+def pin_dominant_key():
+    # Query i aligns with key j*(i); every other score is >= 50 lower, so the softmax bound
+    # |O_i - v_j*| <= 2 (Nk - 1) e^-50 max|v| holds.
+    Nk, d = 16, 16
+    k = np.zeros((1, 1, Nk, d))
+    for j in range(Nk):
+        k[0, 0, j, j] = 1.0
+    q = np.zeros((1, 1, 4, d))
+    targets = [3, 0, 15, 7]
+    for i, j in enumerate(targets):
+        q[0, 0, i, j] = 100.0
+    v = _rand(23, 1, 1, Nk, d)
+    O, lse = A.attention_fp64(q, k, v, 0.5, False)
+    bound = 2 * (Nk - 1) * math.exp(-50) * np.abs(v).max()
+    for i, j in enumerate(targets):
+        _close(O[0, 0, i], v[0, 0, j], bound, "dominant key")
+        assert abs(lse[0, 0, i] - 50.0) <= (Nk - 1) * math.exp(-50) + 1e-14
+
+
+def pin_fully_masked_rows():
+    q = _rand(24, 1, 2, 6, 8)
+    k = _rand(25, 1, 2, 2, 8)
+    v = _rand(26, 1, 2, 2, 8)
+    O, lse = A.attention_fp64(q, k, v, 0.5, True)  # rows 0..3 see no key (j <= i - 4)
+    assert np.all(O[:, :, :4] == 0.0) and np.all(np.isneginf(lse[:, :, :4]))
+    assert np.all(np.isfinite(lse[:, :, 4:]))
+    _close(O[:, :, 4], v[:, :, 0], 0.0, "first visible row sees only key 0")
+    O0, lse0 = A.attention_fp64(q, k[:, :, :0], v[:, :, :0], 0.5, False)
+    assert np.all(O0 == 0.0) and np.all(np.isneginf(lse0)), "Nk = 0 gives empty rows"
+
+
+def pin_default_scale():
+    q = _rand(27, 1, 2, 5, 16)
+    k = _rand(28, 1, 2, 5, 16)
+    v = _rand(29, 1, 2, 5, 16)
+    O, lse = A.attention_fp64(q, k, v, 0.0, True)
+    O2, lse2 = A.attention_fp64(q, k, v, 0.25, True)
+    _close(O, O2, 0.0, "scale 0 means 1/sqrt(d)")
+    _close(lse, lse2, 0.0, "scale 0 means 1/sqrt(d)")
+
+
+# ---- brute force and a library routine -----------------------------------------------------
+
+def _brute(q, k, v, scale, causal):
+    """Scalar Python: O_i = Σ exp(s_ij) v_j / Σ exp(s_ij), lse_i = ln Σ exp(s_ij), no max shift."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    O = np.zeros((B, Hq, Nq, d))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            for i in range(Nq):
+                w = []
+                for j in range(Nk):
+                    if causal and j > i + (Nk - Nq):
+                        continue
+                    s = scale * math.fsum(float(q[b, h, i, t]) * float(k[b, hk, j, t])
+                                          for t in range(d))
+                    w.append((math.exp(s), j))
+                if not w:
+                    continue
+                z = math.fsum(e for e, _ in w)
+                lse[b, h, i] = math.log(z)
+                for t in range(d):
+                    O[b, h, i, t] = math.fsum(e * float(v[b, hk, j, t]) for e, j in w) / z
+    return O, lse
+
+
+def pin_brute_force_small():
+    cases = [(1, 2, 2, 5, 5, 4, True), (2, 4, 2, 3, 9, 8, True), (1, 3, 1, 8, 8, 8, False),
+             (1, 2, 1, 16, 16, 8, True), (1, 2, 2, 6, 3, 4, True)]
+    for n, (B, Hq, Hkv, Nq, Nk, d, causal) in enumerate(cases):
+        q = _rand(100 + n, B, Hq, Nq, d)
+        k = _rand(200 + n, B, Hkv, Nk, d)
+        v = _rand(300 + n, B, Hkv, Nk, d)
+        O, lse = A.attention_fp64(q, k, v, 0.45, causal)
+        Ob, lseb = _brute(q, k, v, 0.45, causal)
+        _close(O, Ob, 1e-12, f"brute force O case {n}")
+        _close(lse, lseb, 1e-12, f"brute force lse case {n}")
+
+
+def pin_scipy_softmax():
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 24, 40, 32
+    q = _rand(30, B, Hq, Nq, d)
+    k = _rand(31, B, Hkv, Nk, d)
+    v = _rand(32, B, Hkv, Nk, d)
+    for causal in (False, True):
+        O, lse = A.attention_fp64(q, k, v, 0.2, causal)
+        vis = _tril_visible(Nq, Nk, causal)
+        for b in range(B):
+            for h in range(Hq):
+                hk = h // (Hq // Hkv)
+                s = 0.2 * np.einsum("id,jd->ij", q[b, h], k[b, hk])
+                s = np.where(vis, s, -np.inf)
+                _close(O[b, h], np.einsum("ij,jd->id", scipy.special.softmax(s, axis=1),
+                                          v[b, hk]), 1e-13, "scipy softmax O")
+                _close(lse[b, h], scipy.special.logsumexp(s, axis=1), 1e-13, "scipy lse")
+
+
+def pin_golden_closed_form():
+    with open(os.path.join(GOLDEN, "closed_form_small.json")) as f:
+        g = json.load(f)
+    q = np.array(g["q"])[None, None]
+    k = np.array(g["k"])[None, None]
+    v = np.array(g["v"])[None, None]
+    for case in g["cases"]:
+        O, lse = A.attention_fp64(q, k, v, g["scale"], case["causal"])
+        _close(O[0, 0], np.array(case["out"]), g["tolerance"], "golden O")
+        _close(lse[0, 0], np.array(case["lse"]), g["tolerance"], "golden lse")
+
+
+# ---- the split-KV model and the FA2 recurrence ---------------------------------------------
+
+def pin_split_combine_equals_single_pass():
+    B, Hq, Hkv, d = 2, 8, 2, 16
+    for Nq, Nk, causal in ((1, 37, True), (4, 16, True), (4, 33, False), (6, 5, True)):
+        q = _rand(40, B, Hq, Nq, d)
+        k = _rand(41, B, Hkv, Nk, d)
+        v = _rand(42, B, Hkv, Nk, d)
+        O, lse = A.attention_fp64(q, k, v, 0.3, causal)
+        for S in sorted({1, 2, 3, min(16, Nk), Nk}):
+            O_s, m_s, l_s = A.splitkv_partials_fp64(q, k, v, 0.3, causal, S)
+            Oc, lsec = A.combine_fp64(O_s, m_s, l_s)
+            _close(Oc, O, 1e-12, f"split combine O (S={S})")
+            _close(lsec, lse, 1e-12, f"split combine lse (S={S})")
+            # partials are locally normalised softmax outputs of their own key chunk
+            L = -(-Nk // S)
+            for s in range(S):
+                k0, k1 = min(s * L, Nk), min((s + 1) * L, Nk)
+                vis = _tril_visible(Nq, Nk, causal)[:, k0:k1]
+                has = vis.any(axis=1)
+                if not causal and k1 > k0:
+                    # a non-causal chunk's partial is plain attention over that chunk alone
+                    Osub, lsub = A.attention_fp64(q, k[:, :, k0:k1], v[:, :, k0:k1], 0.3, False)
+                    _close(O_s[:, :, :, s], Osub, 1e-12, "partial = chunk softmax")
+                    _close(m_s[:, :, :, s] + np.log(l_s[:, :, :, s]), lsub, 1e-12,
+                           "chunk logsumexp")
+                assert np.all(l_s[:, :, ~has, s] == 0) and np.all(np.isneginf(m_s[:, :, ~has, s]))
+                assert np.all(l_s[:, :, has, s] >= 1.0 - 1e-15), "local sum includes exp(0)"
+
+
+def pin_tiled_recurrence_equals_definition():
+    B, Hq, Hkv, d = 1, 4, 2, 8
+    for Nq, Nk in ((19, 19), (7, 23), (23, 7)):
+        q = _rand(50, B, Hq, Nq, d)
+        k = _rand(51, B, Hkv, Nk, d)
+        v = _rand(52, B, Hkv, Nk, d)
+        for causal in (False, True):
+            O, lse = A.attention_fp64(q, k, v, 0.5, causal)
+            for Br, Bc in ((1, 1), (3, 5), (8, 8), (64, 4), (5, 64)):
+                for skip in (False, True):
+                    Ot, lset = A.flash2_tiled_fp64(q, k, v, 0.5, causal, Br, Bc, skip)
+                    _close(Ot, O, 1e-12, f"tiled O Br={Br} Bc={Bc}")
+                    _close(lset, lse, 1e-12, f"tiled lse Br={Br} Bc={Bc}")
+
+
+def pin_decode_rows_equal_prefill_rows():
+    B, Hq, Hkv, Nk, d = 1, 4, 2, 20, 8
+    k = _rand(60, B, Hkv, Nk, d)
+    v = _rand(61, B, Hkv, Nk, d)
+    qfull = _rand(62, B, Hq, Nk, d)
+    Ofull, lsefull = A.attention_fp64(qfull, k, v, 0.35, True)
+    for Nq in (1, 4):
+        O, lse = A.attention_fp64(qfull[:, :, Nk - Nq:], k, v, 0.35, True)
+        _close(O, Ofull[:, :, Nk - Nq:], 1e-15, "decode rows = last prefill rows")
+        _close(lse, lsefull[:, :, Nk - Nq:], 1e-15, "decode lse = last prefill lse")
+
+
+ALL_PINS = [
+    pin_probs_rows_sum_to_one,
+    pin_constant_values,
+    pin_identical_keys_prefix_mean,
+    pin_causal_row_zero,
+    pin_gqa_equals_repeated_heads,
+    pin_key_shift_invariance,
+    pin_permutation_invariance,
+    pin_dominant_key,
+    pin_fully_masked_rows,
+    pin_default_scale,
+    pin_brute_force_small,
+    pin_scipy_softmax,
+    pin_golden_closed_form,
+    pin_split_combine_equals_single_pass,
+    pin_tiled_recurrence_equals_definition,
+    pin_decode_rows_equal_prefill_rows,
+]
