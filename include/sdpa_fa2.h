@@ -42,6 +42,12 @@
 
 #include <stddef.h>
 
+#if defined(__GNUC__)
+#define SDPA_FA2_API __attribute__((visibility("default")))
+#else
+#define SDPA_FA2_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -71,7 +77,7 @@ enum {
  *   out [B, Hq, Nq, d]  bf16 (written, round-to-nearest-even from fp32)
  *   lse [B, Hq, Nq]     fp32 (written unless NULL)
  */
-int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+SDPA_FA2_API int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int d,
              float scale, int causal, void* stream);
 
@@ -79,7 +85,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  * attn_fwd_f32 -- the same operation with float32 q, k, v and out (fp32 arithmetic throughout).
  * Same arguments, layouts and errors as attn_fwd; the tensors hold float32 instead of bf16.
  */
-int attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,
+SDPA_FA2_API int attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse,
                  int B, int Hq, int Hkv, int Nq, int Nk, int d,
                  float scale, int causal, void* stream);
 
@@ -87,7 +93,7 @@ int attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* 
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_splitkv needs:
  *   B*Hq*Nq*n_splits*(d + 2)*4.  Returns 0 for invalid (negative) arguments.
  */
-size_t attn_decode_workspace_bytes(int B, int Hq, int Nq, int d, int n_splits);
+SDPA_FA2_API size_t attn_decode_workspace_bytes(int B, int Hq, int Nq, int d, int n_splits);
 
 /*
  * attn_decode_splitkv -- split-KV attention for few query rows against a long K/V.
@@ -110,13 +116,13 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Nq, int d, int n_splits);
  *     ws_ml float32 [B, Hq, Nq, n_splits, 2]   ((m_s, l_s); empty split: (-inf, 0))
  *   stored back to back, ws_O first.  Calls that share a workspace must be stream ordered.
  */
-int attn_decode_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+SDPA_FA2_API int attn_decode_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
                         void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int Nq, int Nk, int d,
                         float scale, int causal, int n_splits, void* stream);
 
 /* attn_status_string -- a static, NUL-terminated description of a status code. */
-const char* attn_status_string(int status);
+SDPA_FA2_API const char* attn_status_string(int status);
 
 #ifdef __cplusplus
 }

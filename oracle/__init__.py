@@ -8,6 +8,8 @@ Contents:
 
 * ``attention.attention_fp64``  -- the plain definition: matmul, scale, causal mask, softmax,
   matmul, plus the logsumexp of the scaled masked scores.
+* ``attention.attention_rows_fp64`` -- the same definition for a chosen subset of query rows
+  (for sampled checks of problems too large to evaluate whole).
 * ``attention.splitkv_partials_fp64`` / ``attention.combine_fp64`` -- the split-KV decode model:
   per-split locally normalised partial outputs with (max, sum) metadata, and their combine.
 * ``attention.flash2_tiled_fp64`` -- the FlashAttention-2 online-softmax recurrence over Q and K/V
@@ -19,6 +21,7 @@ routine (scipy) and brute force; none is "parity unpinned".
 from .attention import (  # noqa: F401
     attention_fp64,
     attention_probs_fp64,
+    attention_rows_fp64,
     combine_fp64,
     flash2_tiled_fp64,
     splitkv_partials_fp64,

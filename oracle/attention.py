@@ -125,6 +125,31 @@ def attention_fp64(q, k, v, scale: float, causal: bool, row_block: int = 1024
     return out, lse
 
 
+def attention_rows_fp64(q, k, v, scale: float, causal: bool, rows
+                        ) -> Tuple[np.ndarray, np.ndarray]:
+    """Only the query rows ``rows`` (positions in 0..Nq-1, same for every batch and head) of
+    ``attention_fp64``: O [B,Hq,len(rows),d], LSE [B,Hq,len(rows)].  The causal mask uses each
+    row's true position, so sampled rows of a large problem are exact rows of the full result."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
+    scale = _resolve_scale(scale, d)
+    rows = np.asarray(rows, dtype=np.int64)
+    if rows.ndim != 1 or (len(rows) and (rows.min() < 0 or rows.max() >= Nq)):
+        raise ValueError("rows must be positions in [0, Nq)")
+    out = np.zeros((B, Hq, len(rows), d))
+    lse = np.full((B, Hq, len(rows)), NEG_INF)
+    for b in range(B):
+        for hq in range(Hq):
+            hkv = _kv_head(hq, Hq, Hkv)
+            s = _scores(q[b, hq, rows], k[b, hkv], scale)
+            p, m, l = _masked_softmax(s, visible_mask(rows, Nq, Nk, causal))
+            out[b, hq] = _weighted_values(p, v[b, hkv])
+            lse[b, hq] = _row_lse(m, l)
+    return out, lse
+
+
 def attention_probs_fp64(q, k, scale: float, causal: bool) -> np.ndarray:
     """The probability matrix P [B,Hq,Nq,Nk] of the definition (small inputs only)."""
     q = np.asarray(q, dtype=np.float64)

@@ -1,0 +1,175 @@
+"""ctypes binding of ``libsdpa_fa2.so`` (C ABI in ``include/sdpa_fa2.h``).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no fallback: if the library is
+missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsdpa_fa2.so")
+
+ATTN_OK = 0
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+_c_int, _c_float, _vp, _c_size = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_SIGNATURES = {
+    "attn_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+    "attn_fwd_f32": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+    "attn_decode_workspace_bytes": (_c_size, [_c_int] * 5),
+    "attn_decode_splitkv": (_c_int, [_vp] * 6 + [_c_size] + [_c_int] * 6 +
+                            [_c_float, _c_int, _c_int, _vp]),
+    "attn_status_string": (ctypes.c_char_p, [_c_int]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+class AttentionError(RuntimeError):
+    pass
+
+
+def hip_runtimes_mapped():
+    """Distinct libamdhip64 files mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return sorted(paths)
+
+
+def load(path: str = LIB_PATH, require_single_runtime: bool = True) -> ctypes.CDLL:
+    """Load the library once.  torch is imported first so that the library binds to the HIP
+    runtime torch already mapped (both carry the SONAME libamdhip64.so.7)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        import torch  # noqa: F401  (maps torch's HIP runtime before ours is resolved)
+
+        if not os.path.exists(path):
+            raise AttentionError(
+                f"HIP attention library not found at {path}; build it with "
+                "`python -m scaled_dot_product_fa2_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        rts = hip_runtimes_mapped()
+        if require_single_runtime and len(rts) > 1:
+            raise AttentionError(f"two HIP runtimes are mapped into this process: {rts}")
+        _lib = lib
+        return lib
+
+
+def status_string(rc: int) -> str:
+    return load().attn_status_string(rc).decode()
+
+
+def _check_rc(rc: int, what: str):
+    if rc != ATTN_OK:
+        raise AttentionError(f"{what}: {status_string(rc)} (status {rc})")
+
+
+def _ptr(t) -> Optional[int]:
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _stream(device) -> int:
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _validate(q, k, v, dtype):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [batch, heads, seq, head_dim]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, Hq, Nq, d = q.shape
+    return B, Hq, k.shape[1], Nq, k.shape[2], d
+
+
+def attn_fwd(q, k, v, causal: bool = True, scale: float = 0.0, out=None, lse=None,
+             want_lse: bool = True) -> Tuple[object, object]:
+    """Fused attention forward on bf16 [B,H,N,d] tensors; returns (out bf16, lse fp32 or None)."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    rc = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                         float(scale), int(bool(causal)), _stream(q.device))
+    _check_rc(rc, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_f32(q, k, v, causal: bool = True, scale: float = 0.0, out=None, lse=None,
+                 want_lse: bool = True):
+    """The same on float32 tensors (fp32 arithmetic throughout)."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.float32)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    rc = load().attn_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq,
+                             Nk, d, float(scale), int(bool(causal)), _stream(q.device))
+    _check_rc(rc, "attn_fwd_f32")
+    return out, lse
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, Nq: int, d: int, n_splits: int) -> int:
+    return int(load().attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits))
+
+
+def attn_decode_splitkv(q, k, v, n_splits: int, causal: bool = True, scale: float = 0.0,
+                        out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Split-KV decode on bf16 tensors; returns (out, lse, workspace).
+
+    ``workspace`` (a uint8 CUDA tensor of at least ``attn_decode_workspace_bytes`` bytes) may be
+    passed in to reuse memory; it then holds the fp32 partials [B,Hq,Nq,S,d] followed by the
+    (m, l) metadata [B,Hq,Nq,S,2].
+    """
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    need = attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits) if n_splits >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    rc = load().attn_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                                    int(n_splits), _stream(q.device))
+    _check_rc(rc, "attn_decode_splitkv")
+    return out, lse, workspace

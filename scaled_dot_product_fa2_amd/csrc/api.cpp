@@ -1,0 +1,130 @@
+// C ABI of the attention library (declared in include/sdpa_fa2.h): argument validation, then
+// the kernel launches.  Every check runs before anything is enqueued, so an error leaves all
+// outputs untouched.  The library holds no state and never allocates or synchronises.
+#include "sdpa_fa2.h"
+
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int kMaxSeq = 1 << 30;  // keeps every in-kernel index product inside 32/64-bit range
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+// elements of a [n0, n1, n2, n3] tensor; false on overflow
+bool numel4(int n0, int n1, int n2, int n3, uint64_t* out) {
+  uint64_t x = (uint64_t)n0;
+  return mul_ok(x, (uint64_t)n1, &x) && mul_ok(x, (uint64_t)n2, &x) &&
+         mul_ok(x, (uint64_t)n3, &x) && mul_ok(x, 4u, out);  // bytes of fp32 bound the bf16 case
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shared checks.  Returns ATTN_OK and sets *empty when there is nothing to compute.
+int check_common(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, bool* empty) {
+  *empty = false;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d < 0) return ATTN_ERR_SHAPE;
+  if (Nq >= kMaxSeq || Nk >= kMaxSeq) return ATTN_ERR_SHAPE;
+  uint64_t tmp;
+  if (!numel4(B, Hq, Nq, d, &tmp) || !numel4(B, Hkv, Nk, d, &tmp)) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return ATTN_ERR_GQA;
+  if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  if ((uint64_t)B * (uint64_t)Hq * (uint64_t)Nq == 0) {
+    *empty = true;
+    return ATTN_OK;
+  }
+  if (q == nullptr || out == nullptr) return ATTN_ERR_NULL;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+  if (Nk > 0 && (!aligned(k, 16) || !aligned(v, 16))) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+float resolve_scale(float scale, int d) { return scale == 0.f ? 1.0f / sqrtf((float)d) : scale; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+             int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  bool empty;
+  int rc = check_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  const long long blocks = (long long)B * Hq * ((Nq + 127) / 128);
+  if (blocks > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
+  return launch_status(fa::launch_fwd_bf16(q, k, v, out, lse, s, resolve_scale(scale, d),
+                                           causal != 0, (hipStream_t)stream));
+}
+
+int attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                 int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  bool empty;
+  int rc = check_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  if (Hq > 65535 || B > 65535) return ATTN_ERR_SHAPE;
+  const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
+  return launch_status(fa::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v,
+                                          (float*)out, lse, s, resolve_scale(scale, d),
+                                          causal != 0, (hipStream_t)stream));
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Nq, int d, int n_splits) {
+  if (B < 0 || Hq < 0 || Nq < 0 || d < 0 || n_splits < 0) return 0;
+  uint64_t x = (uint64_t)B;
+  if (!mul_ok(x, (uint64_t)Hq, &x) || !mul_ok(x, (uint64_t)Nq, &x) ||
+      !mul_ok(x, (uint64_t)n_splits, &x) || !mul_ok(x, (uint64_t)d + 2u, &x) ||
+      !mul_ok(x, 4u, &x) || x > (uint64_t)SIZE_MAX)
+    return 0;
+  return (size_t)x;
+}
+
+int attn_decode_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq,
+                        int Nk, int d, float scale, int causal, int n_splits, void* stream) {
+  bool empty;
+  int rc = check_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, &empty);
+  if (rc != ATTN_OK) return rc;
+  if (n_splits < 1 || n_splits > (Nk > 1 ? Nk : 1)) return ATTN_ERR_SPLITS;
+  if (empty) return ATTN_OK;
+  const size_t need = attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits);
+  if (need == 0 || workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+  const long long R = (long long)(Hq / Hkv) * Nq;
+  const long long blocks = (long long)B * Hkv * ((R + 31) / 32) * n_splits;
+  const long long rows = (long long)B * Hq * Nq;
+  if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  float* ws_o = (float*)workspace;
+  float* ws_ml = ws_o + (size_t)rows * n_splits * d;
+  const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
+  return launch_status(fa::launch_decode_splitkv(q, k, v, out, lse, ws_o, ws_ml, s,
+                                                 resolve_scale(scale, d), causal != 0, n_splits,
+                                                 (hipStream_t)stream));
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape: negative dimension or size overflow";
+    case ATTN_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
+    case ATTN_ERR_GQA: return "Hq must be a positive multiple of Hkv";
+    case ATTN_ERR_ALIGN: return "tensor base address is not suitably aligned";
+    case ATTN_ERR_SCALE: return "scale must be finite and >= 0 (0 selects 1/sqrt(d))";
+    case ATTN_ERR_SPLITS: return "n_splits must be in [1, max(Nk, 1)]";
+    case ATTN_ERR_WORKSPACE: return "decode workspace is NULL or too small";
+    case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

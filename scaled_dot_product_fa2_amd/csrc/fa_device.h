@@ -1,0 +1,61 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Lane layouts used throughout (64-wide wavefront, measured on gfx950 with an in-bounds probe):
+//   v_mfma_f32_32x32x16_bf16  D = A(32x16) * B(16x32) + C
+//     A[i][k]: lane i + 32*(k/8), bf16 element k%8 of the 8-element operand
+//     B[k][j]: lane j + 32*(k/8), element k%8
+//     C[i][j]: lane j + 32*((i/4)%2), fp32 register 4*(i/8) + i%4   (16 registers)
+//   v_permlane32_swap(x, x) returns {x[l%32], x[l%32 + 32]} in every lane l.
+//   ds_read_b64_tr_b16: within each 16-lane group, output lane i element j is element i%4 of the
+//     four b16 values that source lane 4*j + i/4 of the group addresses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef bf16x4 __attribute__((address_space(3))) lds_bf16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// fp32 accumulate of a 32x32x16 bf16 product; operands travel as raw 32-bit words.
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 values -> one word of two bf16 (round to nearest even), `lo` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum of x over the lane pair (l, l ^ 32); both lanes get the identical result.
+__device__ __forceinline__ float pair32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing 8-byte LDS read (see the layout note above).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+}  // namespace fa

@@ -1,0 +1,31 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the public ABI is
+// include/sdpa_fa2.h).  Arguments are assumed validated by the C-ABI layer: non-empty shapes,
+// d in {64, 128}, Hq % Hkv == 0, aligned pointers, finite positive scale.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct AttnShape {
+  int B, Hq, Hkv, Nq, Nk, d;
+};
+
+// Prefill forward, bf16 tensors (fwd_bf16.hip).
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const AttnShape& s, float scale, bool causal, hipStream_t stream);
+
+// Prefill forward, fp32 tensors (fwd_f32.hip).
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* out,
+                          float* lse, const AttnShape& s, float scale, bool causal,
+                          hipStream_t stream);
+
+// Split-KV decode: split kernel then combine kernel on `stream` (decode.hip).
+// ws_o: fp32 [B, Hq, Nq, n_splits, d]; ws_ml: fp32 [B, Hq, Nq, n_splits, 2].
+hipError_t launch_decode_splitkv(const void* q, const void* k, const void* v, void* out,
+                                 float* lse, float* ws_o, float* ws_ml, const AttnShape& s,
+                                 float scale, bool causal, int n_splits, hipStream_t stream);
+
+}  // namespace fa

@@ -304,6 +304,27 @@ def pin_decode_rows_equal_prefill_rows():
         _close(lse, lsefull[:, :, Nk - Nq:], 1e-15, "decode lse = last prefill lse")
 
 
+def pin_row_subset_equals_full_rows():
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 37, 53, 8
+    q = _rand(70, B, Hq, Nq, d)
+    k = _rand(71, B, Hkv, Nk, d)
+    v = _rand(72, B, Hkv, Nk, d)
+    rows = np.array([0, 1, 17, 36, 5])
+    for causal in (False, True):
+        O, lse = A.attention_fp64(q, k, v, 0.3, causal)
+        Or, lser = A.attention_rows_fp64(q, k, v, 0.3, causal, rows)
+        _close(Or, O[:, :, rows], 1e-15, "row subset O")
+        _close(lser, lse[:, :, rows], 1e-15, "row subset lse")
+    # a row's result depends on its position only through the mask: identical keys give the
+    # prefix mean of the visible values for each sampled position
+    kappa = _rand(73, d)
+    kk = np.broadcast_to(kappa, (B, Hkv, Nk, d)).copy()
+    Or, _ = A.attention_rows_fp64(q, kk, v, 0.3, True, rows)
+    for n, i in enumerate(rows):
+        _close(Or[:, :, n], np.repeat(v[:, :, :i + (Nk - Nq) + 1].mean(axis=2), 2, axis=1),
+               1e-14, "row subset prefix mean")
+
+
 ALL_PINS = [
     pin_probs_rows_sum_to_one,
     pin_constant_values,
@@ -321,4 +342,5 @@ ALL_PINS = [
     pin_split_combine_equals_single_pass,
     pin_tiled_recurrence_equals_definition,
     pin_decode_rows_equal_prefill_rows,
+    pin_row_subset_equals_full_rows,
 ]

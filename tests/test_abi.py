@@ -1,0 +1,150 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header declares, and rejects
+invalid arguments with the documented status codes before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from scaled_dot_product_fa2_amd import binding as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa_fa2.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from scaled_dot_product_fa2_amd import build
+
+        build.build()
+    return fa.load()
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _declared_functions():
+    return re.findall(r"SDPA_FA2_API\s+[\w\s\*]+?\b(attn_\w+)\s*\(", _header())
+
+
+def _status_codes():
+    return {name: int(val) for name, val in re.findall(r"(ATTN_\w+)\s*=\s*(-?\d+)", _header())}
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared_functions()
+    assert sorted(declared) == sorted(fa.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_only_the_abi_is_exported():
+    out = os.popen(f"nm -D --defined-only {fa.LIB_PATH}").read()
+    text = [ln.split()[-1] for ln in out.splitlines() if " T " in ln]
+    assert sorted(text) == sorted(fa.EXPORTED)
+
+
+def test_one_hip_runtime(lib):
+    assert len(fa.hip_runtimes_mapped()) == 1
+
+
+def test_status_strings(lib):
+    codes = _status_codes()
+    assert codes["ATTN_OK"] == 0 and len(set(codes.values())) == len(codes)
+    for name, val in codes.items():
+        s = fa.status_string(val)
+        assert s and s != "unknown status", name
+    assert fa.status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.attn_decode_workspace_bytes(8, 32, 4, 128, 16) == 8 * 32 * 4 * 16 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(8, 32, 1, 64, 3) == 8 * 32 * 1 * 3 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(-1, 32, 1, 64, 3) == 0
+    assert lib.attn_decode_workspace_bytes(2**30, 2**30, 2**30, 128, 2**30) == 0  # overflow
+
+
+C = _status_codes()
+A16 = 0x10000  # a fake, 16-byte-aligned address: never dereferenced, every case below fails first
+GOOD = dict(B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=128, scale=0.0, causal=1)
+
+
+def _fwd(lib, q=A16, k=A16, v=A16, o=A16, lse=None, f32=False, **kw):
+    a = {**GOOD, **kw}
+    fn = lib.attn_fwd_f32 if f32 else lib.attn_fwd
+    return fn(q, k, v, o, lse, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+              a["scale"], a["causal"], None)
+
+
+def _dec(lib, q=A16, k=A16, v=A16, o=A16, lse=None, ws=A16, ws_bytes=1 << 40, S=2, **kw):
+    a = {**GOOD, **kw}
+    return lib.attn_decode_splitkv(q, k, v, o, lse, ws, ws_bytes, a["B"], a["Hq"], a["Hkv"],
+                                   a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], S, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_forward_validation(lib, f32):
+    assert _fwd(lib, f32=f32, B=-1) == C["ATTN_ERR_SHAPE"]
+    assert _fwd(lib, f32=f32, Nk=-5) == C["ATTN_ERR_SHAPE"]
+    assert _fwd(lib, f32=f32, Nq=1 << 30) == C["ATTN_ERR_SHAPE"]
+    assert _fwd(lib, f32=f32, d=96) == C["ATTN_ERR_HEADDIM"]
+    assert _fwd(lib, f32=f32, d=256) == C["ATTN_ERR_HEADDIM"]
+    assert _fwd(lib, f32=f32, Hq=3) == C["ATTN_ERR_GQA"]
+    assert _fwd(lib, f32=f32, Hkv=0) == C["ATTN_ERR_GQA"]
+    assert _fwd(lib, f32=f32, scale=float("nan")) == C["ATTN_ERR_SCALE"]
+    assert _fwd(lib, f32=f32, scale=float("inf")) == C["ATTN_ERR_SCALE"]
+    assert _fwd(lib, f32=f32, scale=-0.5) == C["ATTN_ERR_SCALE"]
+    assert _fwd(lib, f32=f32, q=None) == C["ATTN_ERR_NULL"]
+    assert _fwd(lib, f32=f32, o=None) == C["ATTN_ERR_NULL"]
+    assert _fwd(lib, f32=f32, k=None) == C["ATTN_ERR_NULL"]
+    assert _fwd(lib, f32=f32, q=A16 + 8) == C["ATTN_ERR_ALIGN"]
+    assert _fwd(lib, f32=f32, v=A16 + 2) == C["ATTN_ERR_ALIGN"]
+    assert _fwd(lib, f32=f32, lse=A16 + 2) == C["ATTN_ERR_ALIGN"]
+    # empty problems succeed without touching anything (NULL pointers allowed)
+    assert _fwd(lib, f32=f32, q=None, k=None, v=None, o=None, B=0) == C["ATTN_OK"]
+    assert _fwd(lib, f32=f32, q=None, k=None, v=None, o=None, Nq=0) == C["ATTN_OK"]
+    assert _fwd(lib, f32=f32, q=None, k=None, v=None, o=None, Hq=0, Hkv=0) == C["ATTN_OK"]
+
+
+def test_decode_validation(lib):
+    assert _dec(lib, S=0) == C["ATTN_ERR_SPLITS"]
+    assert _dec(lib, S=9) == C["ATTN_ERR_SPLITS"]           # more splits than keys
+    assert _dec(lib, S=2, Nk=0, k=None, v=None) == C["ATTN_ERR_SPLITS"]
+    assert _dec(lib, ws=None) == C["ATTN_ERR_WORKSPACE"]
+    need = lib.attn_decode_workspace_bytes(1, 4, 8, 128, 2)
+    assert _dec(lib, ws_bytes=need - 1) == C["ATTN_ERR_WORKSPACE"]
+    assert _dec(lib, ws=A16 + 4) == C["ATTN_ERR_ALIGN"]
+    assert _dec(lib, d=80) == C["ATTN_ERR_HEADDIM"]
+    assert _dec(lib, Hq=6, Hkv=4) == C["ATTN_ERR_GQA"]
+    assert _dec(lib, q=None) == C["ATTN_ERR_NULL"]
+    assert _dec(lib, scale=float("-inf")) == C["ATTN_ERR_SCALE"]
+    assert _dec(lib, B=0, q=None, k=None, v=None, o=None, ws=None) == C["ATTN_OK"]
+
+
+def test_binding_requires_the_library(monkeypatch, tmp_path):
+    # the product path has no fallback: a missing library is an error, not a CPU computation
+    monkeypatch.setattr(fa, "_lib", None)
+    with pytest.raises(fa.AttentionError, match="not found"):
+        fa.load(str(tmp_path / "missing.so"))
+
+
+def test_ctypes_signatures_match_header(lib):
+    hdr = _header()
+    for name, (res, args) in fa._SIGNATURES.items():
+        m = re.search(r"SDPA_FA2_API\s+[\w\s\*]+?\b" + name + r"\s*\(([^;]*)\);", hdr, re.S)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip()]
+        assert len(params) == len(args), name
+        for p, a in zip(params, args):
+            p = p.strip()
+            if "*" in p:
+                assert a is ctypes.c_void_p, (name, p)
+            elif p.startswith("size_t"):
+                assert a is ctypes.c_size_t, (name, p)
+            elif p.startswith("float"):
+                assert a is ctypes.c_float, (name, p)
+            else:
+                assert p.startswith("int") and a is ctypes.c_int, (name, p)

@@ -65,6 +65,10 @@ MUTANTS = {
                         np.ones((len(rows), Nk), bool)
                         if not causal else np.arange(Nk)[None, :] < rows[:, None] + (Nk - Nq)),
     "mask_ignored": ("visible_mask", lambda rows, Nq, Nk, causal: np.ones((len(rows), Nk), bool)),
+    "mask_ignores_row_position": ("visible_mask", lambda rows, Nq, Nk, causal:
+                                  np.ones((len(rows), Nk), bool) if not causal else
+                                  np.arange(Nk)[None, :] <= np.arange(len(rows))[:, None]
+                                  + (Nk - Nq)),
     "softmax_over_columns": ("_masked_softmax", _softmax_cols),
     "softmax_unnormalised": ("_masked_softmax", _softmax_unnormalised),
     "lse_without_max": ("_masked_softmax", _softmax_no_max_in_m),
