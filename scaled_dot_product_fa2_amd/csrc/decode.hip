@@ -16,8 +16,9 @@
 //     the 4 waves are merged through LDS at the end into one locally normalised partial.
 //   * The products use v_mfma_f32_32x32x16_bf16 exactly as the prefill kernel does: Sᵀ = K·Qᵀ,
 //     Oᵀ += Vᵀ·Pᵀ with Vᵀ from the transposing LDS read.
-//   * combine kernel: one wave per (batch, query head, row); fixed split order, so the result is
-//     deterministic.
+//   * combine kernel: one wave per (batch, query head, row); the split metadata is read by all
+//     lanes at once and the partial rows are accumulated in a fixed split order, so the result
+//     is deterministic.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -31,13 +32,17 @@ struct DecCfg {
   static constexpr int KB = 32;               // keys per wave block
   static constexpr int NW = 4;                // waves per workgroup
   static constexpr int NT = 64 * NW;
-  static constexpr int ROW = D + 8;           // LDS pitch of a staged K/V row (bf16)
-  static constexpr int WTILE = KB * ROW;      // bf16 elements per staged K or V block
+  // LDS pitches (bf16), each conflict-free for its read pattern on gfx950's 64 x 4-byte banks:
+  // K rows read 16 bytes per lane (pad 16 bytes), V rows read by transposing 8-byte reads
+  // (pad 64 bytes).
+  static constexpr int KROW = D + 8;
+  static constexpr int VROW = D + 32;
+  static constexpr int WTILE = KB * (KROW + VROW);  // one wave's K block + V block (bf16)
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
   static constexpr int NCH = KB * CPR / 64;   // chunks per lane per tensor
   static constexpr int OROW = D + 4;          // fp32 pitch of the cross-wave merge buffer
-  static constexpr int STAGE_BYTES = NW * 2 * WTILE * 2;
-  static constexpr int MERGE_BYTES = NW * 32 * OROW * 4 + NW * 32 * 2 * 4;
+  static constexpr int STAGE_BYTES = NW * WTILE * 2;
+  static constexpr int MERGE_BYTES = NW * 32 * OROW * 4 + NW * 32 * 3 * 4;
   static constexpr int SMEM = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
 };
 
@@ -89,8 +94,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
 
   const uint16_t* Kh = K + ((size_t)b * Hkv + hkv) * Nk * D;
   const uint16_t* Vh = V + ((size_t)b * Hkv + hkv) * Nk * D;
-  uint16_t* kls = (uint16_t*)smem + wave * 2 * C::WTILE;
-  uint16_t* vls = kls + C::WTILE;
+  uint16_t* kls = (uint16_t*)smem + wave * C::WTILE;
+  uint16_t* vls = kls + C::KB * C::KROW;
 
   u32x4 kst[C::NCH], vst[C::NCH];
   auto gload = [&](int kb) {
@@ -113,15 +118,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     for (int i = 0; i < C::NCH; ++i) {
       const int ci = lane + 64 * i;
       const int row = ci / C::CPR, col = (ci % C::CPR) * 8;
-      *(u32x4*)(kls + row * C::ROW + col) = kst[i];
-      *(u32x4*)(vls + row * C::ROW + col) = vst[i];
+      *(u32x4*)(kls + row * C::KROW + col) = kst[i];
+      *(u32x4*)(vls + row * C::VROW + col) = vst[i];
     }
   };
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_run: the lazily moved reference the exponents use; m_true: the exact running max, which
+  // the stored metadata reports
+  float m_run = -INFINITY, m_true = -INFINITY, l_run = 0.f;
   const int tr_g = lane >> 4, tr_j = (lane & 15) >> 2, tr_t = lane & 3;
 
   int kb = wave;
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     f32x16 sc = f32x16{};
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const u32x4 a = *(const u32x4*)(kls + l32 * C::ROW + 16 * c + 8 * h);
+      const u32x4 a = *(const u32x4*)(kls + l32 * C::KROW + 16 * c + 8 * h);
       sc = mfma32x32x16(a, qf[c], sc);
     }
     if (k0 + C::KB - 1 > lim || (CAUSAL && k0 + C::KB - 1 > off)) {
@@ -149,10 +156,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
 #pragma unroll
     for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, sc[rr]);
     mx = pair32_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * scale_log2);
-    const float mb = m_use * scale_log2;
+    m_true = fmaxf(m_true, mx);
+    const bool grow = (mx - m_run) * scale_log2 > kLazyLog2;  // lazy reference max, as in prefill
+    const float m_next = grow ? mx : m_run;
+    const float alpha = grow ? fast_exp2((m_run - m_next) * scale_log2) : 1.f;
+    if (wave_any(grow && m_run != -INFINITY)) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    }
+    m_run = m_next;
+    const float mb = (m_run == -INFINITY ? 0.f : m_run) * scale_log2;
     float rs = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -161,9 +174,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
       rs += p;
     }
     l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
 
     u32x4 pb[2];
 #pragma unroll
@@ -178,9 +188,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         const int row0 = 16 * mm + 4 * h + tr_j;
-        const u32x2 lo = lds_read_tr16(vls + row0 * C::ROW + col);
-        const u32x2 hi = lds_read_tr16(vls + (row0 + 8) * C::ROW + col);
-        oacc[db] = mfma32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[mm], oacc[db]);
+        const bf16x8 a = lds_read_tr16_pair(vls + row0 * C::VROW + col,
+                                            vls + (row0 + 8) * C::VROW + col);
+        oacc[db] = mfma32x32x16(a, pb[mm], oacc[db]);
       }
     }
     wave_lds_sync();  // this block's LDS reads precede the next block's writes
@@ -189,8 +199,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   // merge the 4 waves' (m, l, Oᵀ) into one locally normalised partial for the split
   const float l_tot = pair32_sum(l_run);
   __syncthreads();
-  float* ocb = (float*)smem;            // [NW][32][OROW] unnormalised Oᵀ rows
-  float* mlb = ocb + C::NW * 32 * C::OROW;  // [NW][32][2]  (max in score units, sum)
+  float* ocb = (float*)smem;                // [NW][32][OROW] unnormalised Oᵀ rows
+  float* mlb = ocb + C::NW * 32 * C::OROW;  // [NW][32][3]: exact max, reference max, sum
+                                            // (score units; the sum is against the reference)
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -199,8 +210,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
           f32x4{oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2],
                 oacc[db][4 * g4 + 3]};
   if (h == 0) {
-    mlb[(wave * 32 + l32) * 2 + 0] = m_run;
-    mlb[(wave * 32 + l32) * 2 + 1] = l_tot;
+    mlb[(wave * 32 + l32) * 3 + 0] = m_true;
+    mlb[(wave * 32 + l32) * 3 + 1] = m_run;
+    mlb[(wave * 32 + l32) * 3 + 2] = l_tot;
   }
   __syncthreads();
 
@@ -210,16 +222,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   if (rr < R) {
     const int g2 = rr / Nq, qi2 = rr - g2 * Nq;
     const int hq2 = hkv * G + g2;
+    // M = exact max of the split; each wave's sum and accumulator are re-expressed against it
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < C::NW; ++w)
-      if (mlb[(w * 32 + qr) * 2 + 1] > 0.f) M = fmaxf(M, mlb[(w * 32 + qr) * 2]);
+      if (mlb[(w * 32 + qr) * 3 + 2] > 0.f) M = fmaxf(M, mlb[(w * 32 + qr) * 3]);
     float ew[C::NW];
     float Lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < C::NW; ++w) {
-      const float lw = mlb[(w * 32 + qr) * 2 + 1];
-      ew[w] = lw > 0.f ? fast_exp2((mlb[(w * 32 + qr) * 2] - M) * scale_log2) : 0.f;
+      const float lw = mlb[(w * 32 + qr) * 3 + 2];
+      ew[w] = lw > 0.f ? fast_exp2((mlb[(w * 32 + qr) * 3 + 1] - M) * scale_log2) : 0.f;
       Lsum += ew[w] * lw;
     }
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
@@ -240,34 +253,63 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   }
 }
 
+// max / sum over the 64 lanes of a wave (every lane gets the result)
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// One wave per output row (batch, query head, position).  Lane s reads the metadata of split s
+// (64 splits per pass), so all metadata loads are in flight together; the weights
+// w_s = l_s exp(m_s - M) are then broadcast lane by lane while the partial rows stream in.
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ wsO,
-                                                            const float* __restrict__ wsML,
-                                                            uint16_t* __restrict__ O,
-                                                            float* __restrict__ LSE, int rows,
-                                                            int S) {
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ wsO,
+                                                           const float* __restrict__ wsML,
+                                                           uint16_t* __restrict__ O,
+                                                           float* __restrict__ LSE, int rows,
+                                                           int S) {
   constexpr int E = D / 64;  // head-dim elements per lane
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
   if (row >= rows) return;
-  const float* ml = wsML + (size_t)row * S * 2;
+  const f32x2* ml = (const f32x2*)(wsML + (size_t)row * S * 2);
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s)
-    if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const f32x2 v = (s0 + lane < S) ? ml[s0 + lane] : f32x2{-INFINITY, 0.f};
+    M = fmaxf(M, v[1] > 0.f ? v[0] : -INFINITY);
+  }
+  M = wave_max(M);
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float W = 0.f;
   const float* src = wsO + (size_t)row * S * D + lane * E;
-  for (int s = 0; s < S; ++s) {
-    const float l = ml[2 * s + 1];
-    if (l > 0.f) {
-      const float w = l * fast_exp2((ml[2 * s] - M) * kLog2e);
-      W += w;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(w, src[(size_t)s * D + e], acc[e]);
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int n = min(64, S - s0);
+    const f32x2 v = (lane < n) ? ml[s0 + lane] : f32x2{-INFINITY, 0.f};
+    const float w = v[1] > 0.f ? v[1] * fast_exp2((v[0] - M) * kLog2e) : 0.f;
+    W += w;
+#pragma unroll 8
+    for (int j = 0; j < n; ++j) {
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                     __builtin_bit_cast(int, w), j));
+      const float* p = src + (size_t)(s0 + j) * D;
+      if constexpr (E == 2) {
+        const f32x2 o = *(const f32x2*)p;
+        acc[0] = fmaf(wj, o[0], acc[0]);
+        acc[1] = fmaf(wj, o[1], acc[1]);
+      } else {
+        acc[0] = fmaf(wj, p[0], acc[0]);
+      }
     }
   }
+  W = wave_sum(W);
   const float inv = W > 0.f ? 1.f / W : 0.f;
   uint16_t* dst = O + (size_t)row * D + lane * E;
   if constexpr (E == 2) {
@@ -288,13 +330,13 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, float*
   const int nrg = (R + 31) / 32;
   const long long blocks = (long long)sh.B * sh.Hkv * nrg * S;
   const long long rows = (long long)sh.B * sh.Hq * sh.Nq;
-  if (blocks > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(C::NT), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws_o,
                      ws_ml, sh.Hq, sh.Hkv, sh.Nq, sh.Nk, S, L, nrg, scale, scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)rows), dim3(64), 0,
                      stream, (const float*)ws_o, (const float*)ws_ml, (uint16_t*)out, lse,
                      (int)rows, S);
   return hipGetLastError();

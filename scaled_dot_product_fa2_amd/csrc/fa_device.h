@@ -53,9 +53,26 @@ __device__ __forceinline__ float pair32_sum(float x) {
 }
 
 // Transposing 8-byte LDS read (see the layout note above).
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-  return __builtin_bit_cast(u32x2, v);
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
 }
+
+// The 8-element MFMA operand made of two transposing reads (first read -> elements 0..3).
+__device__ __forceinline__ bf16x8 lds_read_tr16_pair(const uint16_t* p0, const uint16_t* p1) {
+  return __builtin_shufflevector(lds_read_tr16(p0), lds_read_tr16(p1), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Lazy rescaling of the online softmax: the running max m that exponents are taken against is
+// only moved when a block's max exceeds it by more than this many powers of two, so the
+// probabilities stay below 2^kLazyLog2 and the accumulator is rarely rescaled.  O and l always
+// share the same reference max, so the final O / l is unchanged.
+constexpr float kLazyLog2 = 8.0f;
+
+// 64 lanes of the wave vote: true when the predicate holds in any active lane.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 }  // namespace fa

@@ -17,7 +17,9 @@
 //   * Oᵀ += Vᵀ·Pᵀ on the same MFMA: Pᵀ is the B operand straight from the score registers (packed
 //     to bf16); the matching key order of Vᵀ comes from the transposing LDS read ds_read_b64_tr_b16,
 //     so V stays row-major in LDS.  Every Oᵀ accumulator of a lane belongs to its own query, so the
-//     rescale by exp2((m_old - m_new)·scale·log2e) is a per-lane scalar multiply.
+//     rescale by exp2((m_old - m_new)·scale·log2e) is a per-lane scalar multiply, and it is only
+//     done when some row's max grew by more than 2^8 (lazy rescaling; O and l keep one reference).
+//   * K and V blocks use different LDS row pitches, each conflict-free for its own read pattern.
 //   * K/V blocks are staged global -> registers (16-byte coalesced loads, next block prefetched
 //     during the current block's math) -> LDS (double buffered, one barrier per block).
 //   * Workgroups are ordered heaviest-first under the causal mask, and all query blocks of one
@@ -35,8 +37,16 @@ struct FwdCfg {
   static constexpr int BR = 128;               // query rows per workgroup
   static constexpr int BC = 64;                // keys per K/V block
   static constexpr int NT = 256;               // threads per workgroup (4 waves)
-  static constexpr int ROW = D + 8;            // LDS row pitch in bf16 (16-byte pad)
-  static constexpr int TILE = BC * ROW;        // bf16 elements per staged K or V block
+  // LDS row pitches (bf16).  gfx950 LDS serves 256 B per clock from 64 four-byte banks:
+  //  * K rows are read 16 bytes per lane, 16 lanes (16 rows) per clock: a pitch of 4 (mod 64)
+  //    words spreads those rows over all banks -> pad 16 bytes.
+  //  * V rows are read by the transposing 8-byte reads, 32 lanes = 4 rows x 64 bytes per clock:
+  //    a pitch of 16 (mod 64) words puts the 4 rows in disjoint bank quarters -> pad 64 bytes.
+  static constexpr int KROW = D + 8;
+  static constexpr int VROW = D + 32;
+  static constexpr int KTILE = BC * KROW;      // bf16 elements per staged K block
+  static constexpr int VTILE = BC * VROW;      // bf16 elements per staged V block
+  static constexpr int STAGE = KTILE + VTILE;  // one K block + one V block
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int NCH = BC * CPR / NT;    // chunks per thread per tensor
   static_assert(BC * CPR % NT == 0, "staging must divide evenly");
@@ -62,7 +72,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq,
     int Hkv, int Nq, int Nk, int nqt, float scale, float scale_log2) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -109,14 +119,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     }
   };
   auto swrite = [&](int buf) {
-    uint16_t* ks = smem + buf * 2 * C::TILE;
-    uint16_t* vs = ks + C::TILE;
+    uint16_t* ks = smem + buf * C::STAGE;
+    uint16_t* vs = ks + C::KTILE;
 #pragma unroll
     for (int i = 0; i < C::NCH; ++i) {
       const int ci = tid + C::NT * i;
       const int row = ci / C::CPR, col = (ci % C::CPR) * 8;
-      *(u32x4*)(ks + row * C::ROW + col) = kst[i];
-      *(u32x4*)(vs + row * C::ROW + col) = vst[i];
+      *(u32x4*)(ks + row * C::KROW + col) = kst[i];
+      *(u32x4*)(vs + row * C::VROW + col) = vst[i];
     }
   };
 
@@ -137,8 +147,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) gload(t + 1);
-    const uint16_t* ks = smem + buf * 2 * C::TILE;
-    const uint16_t* vs = ks + C::TILE;
+    const uint16_t* ks = smem + buf * C::STAGE;
+    const uint16_t* vs = ks + C::KTILE;
     const int k0 = t * C::BC;
     const bool active = (qw0 < Nq) && (!CAUSAL || k0 <= qw0 + 31 + off);
     if (active) {
@@ -149,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         s[kb] = f32x16{};
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
-          const u32x4 a = *(const u32x4*)(ks + (32 * kb + l32) * C::ROW + 16 * c + 8 * h);
+          const u32x4 a = *(const u32x4*)(ks + (32 * kb + l32) * C::KROW + 16 * c + 8 * h);
           s[kb] = mfma32x32x16(a, qf[c], s[kb]);
         }
       }
@@ -165,17 +175,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
             if (key > lim) s[kb][r] = -INFINITY;
           }
       }
-      // online softmax: running max, rescale, exponentiate, running sum (per lane = per query)
+      // online softmax (per lane = per query): block max, lazily moved reference max, rescale,
+      // exponentiate, running sum
       float mx = s[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = pair32_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * scale_log2);
-      const float mb = m_use * scale_log2;
+      const bool grow = (mx - m_run) * scale_log2 > kLazyLog2;  // false while both are -inf
+      const float m_next = grow ? mx : m_run;
+      const float alpha = grow ? fast_exp2((m_run - m_next) * scale_log2) : 1.f;
+      if (wave_any(grow && m_run != -INFINITY)) {  // an already-started row moves its max
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      }
+      m_run = m_next;
+      const float mb = (m_run == -INFINITY ? 0.f : m_run) * scale_log2;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -186,9 +202,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
           rs += p;
         }
       l_run = l_run * alpha + rs;  // lane-half partial; the partner half is added at the end
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
 
       // Pᵀ as B operands: block kb, 16-key group mm uses score registers 8mm .. 8mm+7
       u32x4 pb[4];
@@ -210,9 +223,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
         for (int m4 = 0; m4 < 4; ++m4) {
           const int row0 = 16 * m4 + 4 * h + tr_j;
-          const u32x2 lo = lds_read_tr16(vs + row0 * C::ROW + col);
-          const u32x2 hi = lds_read_tr16(vs + (row0 + 8) * C::ROW + col);
-          oacc[db] = mfma32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[m4], oacc[db]);
+          const bf16x8 a = lds_read_tr16_pair(vs + row0 * C::VROW + col,
+                                              vs + (row0 + 8) * C::VROW + col);
+          oacc[db] = mfma32x32x16(a, pb[m4], oacc[db]);
         }
       }
     }
