@@ -27,7 +27,9 @@
  *          A query row with no visible key gets out = 0 and lse = -inf.
  * LSE:     lse[b,h,i] = ln sum_j exp(scale * q_i . k_j) over visible j (natural log), float32.
  *          `lse` may be NULL, in which case it is not written.
- * Shapes:  every dimension must be >= 0; d must be 64 or 128.  An empty problem (B*Hq*Nq == 0)
+ * Shapes:  every dimension must be >= 0; d must be 64 or 128; one K/V head slice must stay below
+ *          4 GiB ((Nk + 128) * d * 2 < 2^32, i.e. Nk < 16,777,088 at d = 128) and Nq, Nk < 2^30.
+ *          An empty problem (B*Hq*Nq == 0)
  *          returns ATTN_OK without launching anything.  Nk == 0 is allowed (all rows empty).
  * Pointers: q/out must be non-NULL when B*Hq*Nq > 0, k/v when additionally Nk > 0; q, k, v, out
  *          and the workspace must be 16-byte aligned, lse 4-byte aligned.
@@ -55,7 +57,7 @@ extern "C" {
 enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = -2,     /* a negative dimension, or a size that overflows */
+  ATTN_ERR_SHAPE = -2,     /* a negative dimension, a size that overflows, or a too-long K/V */
   ATTN_ERR_HEADDIM = -3,   /* d is not 64 or 128 */
   ATTN_ERR_GQA = -4,       /* Hkv < 1 while Hq > 0, or Hq % Hkv != 0 */
   ATTN_ERR_ALIGN = -5,     /* a tensor base address is not suitably aligned */

@@ -33,6 +33,9 @@ int check_common(const void* q, const void* k, const void* v, const void* out, c
   uint64_t tmp;
   if (!numel4(B, Hq, Nq, d, &tmp) || !numel4(B, Hkv, Nk, d, &tmp)) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  // one (batch, head) slice of K or V, plus one block of overrun, must be addressable by the
+  // kernels' 32-bit buffer offsets
+  if (((uint64_t)Nk + 128u) * (uint64_t)d * 2u > 0xffffffffull) return ATTN_ERR_SHAPE;
   if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return ATTN_ERR_GQA;
   if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
   if ((uint64_t)B * (uint64_t)Hq * (uint64_t)Nq == 0) {

@@ -72,6 +72,24 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, u32x4 b, f32x16 c) {
 // share the same reference max, so the final O / l is unchanged.
 constexpr float kLazyLog2 = 8.0f;
 
+// Buffer resource covering `bytes` bytes from `base` (raw addressing, no stride).  Buffer loads
+// through it read zero past the end, which is how K/V rows beyond the sequence are filled.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane from `rsrc` at byte offset `voff` straight into LDS: lane i's bytes land at
+// `lds_base` + 16 i (`lds_base` must be the same for the whole wave).
+__device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t rsrc, void* lds_base,
+                                            uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory loads (including LDS-direct ones) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // 64 lanes of the wave vote: true when the predicate holds in any active lane.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 

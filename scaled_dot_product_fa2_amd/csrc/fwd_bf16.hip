@@ -19,9 +19,11 @@
 //     so V stays row-major in LDS.  Every Oᵀ accumulator of a lane belongs to its own query, so the
 //     rescale by exp2((m_old - m_new)·scale·log2e) is a per-lane scalar multiply, and it is only
 //     done when some row's max grew by more than 2^8 (lazy rescaling; O and l keep one reference).
-//   * K and V blocks use different LDS row pitches, each conflict-free for its own read pattern.
-//   * K/V blocks are staged global -> registers (16-byte coalesced loads, next block prefetched
-//     during the current block's math) -> LDS (double buffered, one barrier per block).
+//   * K/V blocks go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane, no
+//     register staging), double buffered: the next block's loads are issued right after the
+//     barrier that publishes the current one.  Rows past the end of K/V read as zero through the
+//     buffer range check.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled, K and
+//     V each with the swizzle that makes its read pattern conflict-free on the 64 LDS banks.
 //   * Workgroups are ordered heaviest-first under the causal mask, and all query blocks of one
 //     (batch, head) are kept on one XCD so their shared K/V stays in that XCD's L2.
 #include "fa_device.h"
@@ -34,23 +36,29 @@ namespace {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BR = 128;               // query rows per workgroup
-  static constexpr int BC = 64;                // keys per K/V block
-  static constexpr int NT = 256;               // threads per workgroup (4 waves)
-  // LDS row pitches (bf16).  gfx950 LDS serves 256 B per clock from 64 four-byte banks:
-  //  * K rows are read 16 bytes per lane, 16 lanes (16 rows) per clock: a pitch of 4 (mod 64)
-  //    words spreads those rows over all banks -> pad 16 bytes.
-  //  * V rows are read by the transposing 8-byte reads, 32 lanes = 4 rows x 64 bytes per clock:
-  //    a pitch of 16 (mod 64) words puts the 4 rows in disjoint bank quarters -> pad 64 bytes.
-  static constexpr int KROW = D + 8;
-  static constexpr int VROW = D + 32;
-  static constexpr int KTILE = BC * KROW;      // bf16 elements per staged K block
-  static constexpr int VTILE = BC * VROW;      // bf16 elements per staged V block
-  static constexpr int STAGE = KTILE + VTILE;  // one K block + one V block
-  static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int NCH = BC * CPR / NT;    // chunks per thread per tensor
-  static_assert(BC * CPR % NT == 0, "staging must divide evenly");
+  static constexpr int BR = 128;                     // query rows per workgroup
+  static constexpr int BC = 64;                      // keys per K/V block
+  static constexpr int NT = 256;                     // threads per workgroup (4 waves)
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int TILE = BC * D;                // bf16 elements per K or V block
+  static constexpr int STAGE = 2 * TILE;             // one K block + one V block
+  static constexpr int RPL = 64 / CPR;               // rows covered by one wave-wide 1 KB load
+  static constexpr int LPW = BC / RPL / 4;           // 1 KB loads per wave per tensor per block
+  static_assert(BC % (4 * RPL) == 0, "staging must divide evenly");
 };
+
+// Physical 16-byte chunk of logical chunk c in row `row` (XOR swizzle, an involution).
+// K rows are read 16 lanes = 16 consecutive rows at one logical chunk per LDS cycle; V rows by
+// transposing reads, 32 lanes = 4 consecutive rows x 4 consecutive chunks per cycle.  Each
+// swizzle maps those sets onto 16 distinct bank quads.
+template <int D>
+__device__ __forceinline__ int k_chunk(int row, int c) {
+  return D == 128 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
+}
+template <int D>
+__device__ __forceinline__ int v_chunk(int row, int c) {
+  return D == 128 ? (c ^ ((row & 3) << 2)) : (c ^ (((row >> 1) & 1) << 2));
+}
 
 // Block index -> (batch*head, query block).  Heaviest query blocks first (the last ones under a
 // causal mask); when B*H is a multiple of 8 the blocks of a head go to one XCD (the dispatcher
@@ -72,9 +80,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq,
     int Hkv, int Nq, int Nk, int nqt, float scale, float scale_log2) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int BH = gridDim.x / nqt;
   int bh, qt;
@@ -86,8 +95,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int qw0 = q_tile0 + wave * 32;  // first query row of this wave
   const int my_q = qw0 + l32;
 
-  const uint16_t* Kh = K + (size_t)(b * Hkv + hkv) * Nk * D;
-  const uint16_t* Vh = V + (size_t)(b * Hkv + hkv) * Nk * D;
+  const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + (size_t)(b * Hkv + hkv) * Nk * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + (size_t)(b * Hkv + hkv) * Nk * D, kv_bytes);
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(Nq - 1, q_tile0 + C::BR - 1) + off + 1);
@@ -102,31 +112,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       qf[c] = (my_q < Nq) ? *(const u32x4*)(qrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  u32x4 kst[C::NCH], vst[C::NCH];
-  auto gload = [&](int t) {
+  // This lane's slot in the wave's 1 KB direct loads: row within the load, physical chunk.
+  const int ld_row = lane / C::CPR, ld_chunk = lane % C::CPR;
+  auto issue_loads = [&](int t, int buf) {
+    uint16_t* kbase = smem + buf * C::STAGE;
+    uint16_t* vbase = kbase + C::TILE;
 #pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
-      const int ci = tid + C::NT * i;
-      const int row = ci / C::CPR, col = (ci % C::CPR) * 8;
-      const int key = t * C::BC + row;
-      if (key < Nk) {  // rows past the end read as zero (and are masked below)
-        kst[i] = *(const u32x4*)(Kh + (size_t)key * D + col);
-        vst[i] = *(const u32x4*)(Vh + (size_t)key * D + col);
-      } else {
-        kst[i] = u32x4{0u, 0u, 0u, 0u};
-        vst[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-    uint16_t* ks = smem + buf * C::STAGE;
-    uint16_t* vs = ks + C::KTILE;
-#pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
-      const int ci = tid + C::NT * i;
-      const int row = ci / C::CPR, col = (ci % C::CPR) * 8;
-      *(u32x4*)(ks + row * C::KROW + col) = kst[i];
-      *(u32x4*)(vs + row * C::VROW + col) = vst[i];
+    for (int i = 0; i < C::LPW; ++i) {
+      const int blk = wave * C::LPW + i;  // which 1 KB piece of the block
+      const int row = blk * C::RPL + ld_row;
+      const uint32_t rowoff = (uint32_t)(t * C::BC + row) * (D * 2);
+      load_lds_16(krs, kbase + blk * 512, rowoff + 16u * k_chunk<D>(row, ld_chunk));
+      load_lds_16(vrs, vbase + blk * 512, rowoff + 16u * v_chunk<D>(row, ld_chunk));
     }
   };
 
@@ -138,30 +135,33 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // transposing-read coordinates of this lane (see the layout note in fa_device.h)
   const int tr_g = lane >> 4, tr_j = (lane & 15) >> 2, tr_t = lane & 3;
 
-  if (n_tiles > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
+  if (n_tiles > 0) issue_loads(0, 0);
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(t + 1);
+    wait_vmem();       // this wave's share of block t has landed in LDS
+    __syncthreads();   // ... and everyone's; everyone is also done reading the other buffer
+    if (t + 1 < n_tiles) issue_loads(t + 1, buf ^ 1);
     const uint16_t* ks = smem + buf * C::STAGE;
-    const uint16_t* vs = ks + C::KTILE;
+    const uint16_t* vs = ks + C::TILE;
     const int k0 = t * C::BC;
     const bool active = (qw0 < Nq) && (!CAUSAL || k0 <= qw0 + 31 + off);
     if (active) {
-      // Sᵀ = K·Qᵀ for two 32-key halves of the block
+      // Sᵀ = K·Qᵀ for two 32-key halves of the block; all K operands are read up front
+      u32x4 kop[2][D / 16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 32 * kb + l32;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+          kop[kb][c] = *(const u32x4*)(ks + row * D + 8 * k_chunk<D>(row, 2 * c + h));
+      }
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const u32x4 a = *(const u32x4*)(ks + (32 * kb + l32) * C::KROW + 16 * c + 8 * h);
-          s[kb] = mfma32x32x16(a, qf[c], s[kb]);
-        }
+        for (int c = 0; c < D / 16; ++c) s[kb] = mfma32x32x16(kop[kb][c], qf[c], s[kb]);
       }
       // mask keys past Nk and, on diagonal blocks, keys after this row's last visible key
       const bool need_mask = (k0 + C::BC > Nk) || (CAUSAL && (k0 + C::BC - 1 > qw0 + off));
@@ -219,18 +219,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       // 32kb + 16mm + 8c + 4h + j, matching the score register order above.
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int col = 32 * db + 16 * (tr_g & 1) + 4 * tr_t;
+        const int chunk = 4 * db + 2 * (tr_g & 1) + (tr_t >> 1);
+        const int within = 4 * (tr_t & 1);
+        bf16x8 vop[4];
 #pragma unroll
         for (int m4 = 0; m4 < 4; ++m4) {
-          const int row0 = 16 * m4 + 4 * h + tr_j;
-          const bf16x8 a = lds_read_tr16_pair(vs + row0 * C::VROW + col,
-                                              vs + (row0 + 8) * C::VROW + col);
-          oacc[db] = mfma32x32x16(a, pb[m4], oacc[db]);
+          const int r0 = 16 * m4 + 4 * h + tr_j, r1 = r0 + 8;
+          vop[m4] = lds_read_tr16_pair(vs + r0 * D + 8 * v_chunk<D>(r0, chunk) + within,
+                                       vs + r1 * D + 8 * v_chunk<D>(r1, chunk) + within);
         }
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) oacc[db] = mfma32x32x16(vop[m4], pb[m4], oacc[db]);
       }
     }
-    if (t + 1 < n_tiles) swrite(buf ^ 1);
-    __syncthreads();
   }
 
   // epilogue: one 1/l per row, bf16 output, natural-log logsumexp
