@@ -103,7 +103,7 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, void* out, 
   if (need == 0 || workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
   const long long R = (long long)(Hq / Hkv) * Nq;
-  const long long blocks = (long long)B * Hkv * ((R + 31) / 32) * n_splits;
+  const long long blocks = (long long)B * Hkv * ((R + 15) / 16) * n_splits;
   const long long rows = (long long)B * Hq * Nq;
   if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   float* ws_o = (float*)workspace;

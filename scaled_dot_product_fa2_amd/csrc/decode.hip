@@ -8,14 +8,15 @@
 // rows so that the K/V it streams is read once for all of them.
 //
 // gfx950 mapping:
-//   * split kernel: one workgroup (4 waves) per (batch, KV head, row group of 32, split).  The
-//     32 "query" columns of the MFMA are the Hq/Hkv query heads x Nq rows that share the KV head,
+//   * split kernel: one workgroup (4 waves) per (batch, KV head, row group of 16, split).  The
+//     16 "query" columns of the MFMA are the Hq/Hkv query heads x Nq rows that share the KV head,
 //     so every K/V byte of the split is read from HBM exactly once.  Each wave streams its own
-//     32-key blocks (block w, w+4, ...) through a wave-private LDS slice with 16-byte coalesced
-//     loads, prefetching its next block while it computes, and keeps its own running (m, l, Oᵀ);
-//     the 4 waves are merged through LDS at the end into one locally normalised partial.
-//   * The products use v_mfma_f32_32x32x16_bf16 exactly as the prefill kernel does: Sᵀ = K·Qᵀ,
-//     Oᵀ += Vᵀ·Pᵀ with Vᵀ from the transposing LDS read.
+//     32-key blocks (block w, w+4, ...) with non-temporal 16-byte buffer loads whose range ends
+//     at the split (later keys read as zero), keeps two blocks in flight in registers, stages
+//     the current one in a wave-private LDS slice, and keeps its own running (m, l, Oᵀ); the 4
+//     waves are merged through LDS at the end into one locally normalised partial.
+//   * Products on v_mfma_f32_16x16x32_bf16: Sᵀ = K·Qᵀ, then Oᵀ += Vᵀ·Pᵀ with Pᵀ taken straight
+//     from the score registers and Vᵀ from the transposing LDS read.
 //   * combine kernel: one wave per (batch, query head, row); the split metadata is read by all
 //     lanes at once and the partial rows are accumulated in a fixed split order, so the result
 //     is deterministic.
@@ -30,21 +31,30 @@ namespace {
 template <int D>
 struct DecCfg {
   static constexpr int KB = 32;               // keys per wave block
+  static constexpr int QC = 16;               // query columns per workgroup (MFMA N)
   static constexpr int NW = 4;                // waves per workgroup
   static constexpr int NT = 64 * NW;
-  // LDS pitches (bf16), each conflict-free for its read pattern on gfx950's 64 x 4-byte banks:
-  // K rows read 16 bytes per lane (pad 16 bytes), V rows read by transposing 8-byte reads
-  // (pad 64 bytes).
-  static constexpr int KROW = D + 8;
-  static constexpr int VROW = D + 32;
-  static constexpr int WTILE = KB * (KROW + VROW);  // one wave's K block + V block (bf16)
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int NCH = KB * CPR / 64;   // chunks per lane per tensor
+  static constexpr int NCH = KB * CPR / 64;   // chunks per lane per tensor per block
+  static constexpr int WTILE = 2 * KB * D;    // one wave's K block + V block (bf16)
   static constexpr int OROW = D + 4;          // fp32 pitch of the cross-wave merge buffer
   static constexpr int STAGE_BYTES = NW * WTILE * 2;
-  static constexpr int MERGE_BYTES = NW * 32 * OROW * 4 + NW * 32 * 3 * 4;
+  static constexpr int MERGE_BYTES = NW * QC * OROW * 4 + NW * QC * 3 * 4;
   static constexpr int SMEM = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
 };
+
+// LDS placement of a wave's staged block: rows unpadded, 16-byte chunks XOR-swizzled so that
+// both read patterns are conflict-free on the 64 banks.  K operand reads take 16 consecutive
+// rows at one chunk per cycle; the transposing V reads take 8 consecutive rows x 2 adjacent
+// chunks per cycle.
+template <int D>
+__device__ __forceinline__ int dk_chunk(int row, int c) {
+  return D == 128 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
+}
+template <int D>
+__device__ __forceinline__ int dv_chunk(int row, int c) {
+  return D == 128 ? (c ^ ((row & 7) << 1)) : (c ^ (((row >> 1) & 3) << 1));
+}
 
 // Orders this wave's LDS writes before its later LDS reads of other lanes' data.  A wave's LDS
 // operations complete in issue order, so only compiler reordering has to be prevented.
@@ -52,6 +62,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// max / sum over the four lanes {q, q+16, q+32, q+48} (every one of them gets the result)
+__device__ __forceinline__ float quad_max(float x) {
+  x = pair32_max(x);
+  return fmaxf(x, __shfl_xor(x, 16));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  x = pair32_sum(x);
+  return x + __shfl_xor(x, 16);
 }
 
 template <int D, bool CAUSAL>
@@ -63,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
+  const int grp = lane >> 4, l16 = lane & 15;  // 16-lane group, query column
   int n = blockIdx.x;
   const int s = n % S;
   n /= S;
@@ -74,7 +94,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const int off = Nk - Nq;
 
   // this lane's query column: row r of the KV head's group = (query head offset g, position qi)
-  const int r = rg * 32 + l32;
+  const int r = rg * C::QC + l16;
   const bool row_ok = r < R;
   const int g = row_ok ? r / Nq : 0;
   const int qi = row_ok ? r - g * Nq : 0;
@@ -84,141 +104,153 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const int nkb = (ks1 - ks0 + C::KB - 1) / C::KB;
   const int lim = CAUSAL ? min(ks1 - 1, qi + off) : ks1 - 1;  // last visible key of this row
 
-  u32x4 qf[D / 16];
+  // buffer resources covering exactly this split's keys: rows past the split read as zero
+  const size_t split_off = (((size_t)b * Hkv + hkv) * Nk + ks0) * D;
+  const uint32_t split_bytes = (uint32_t)(ks1 - ks0) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + split_off, split_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + split_off, split_bytes);
+  uint16_t* kls = (uint16_t*)smem + wave * C::WTILE;
+  uint16_t* vls = kls + C::KB * D;
+
+  // K/V blocks travel HBM -> registers (16-byte coalesced loads, two blocks in flight per wave)
+  // -> this wave's LDS slice -> MFMA operands.  Chunk i of a lane is byte
+  // (32 kb + lane / CPR + i * 64 / CPR) * 2D + (lane % CPR) * 16 of the split.
+  const uint32_t lane_off = (uint32_t)(lane / C::CPR) * (D * 2) + (uint32_t)(lane % C::CPR) * 16;
+  auto gload = [&](u32x4 (&kst)[C::NCH], u32x4 (&vst)[C::NCH], int kb) {
+    const uint32_t voff = lane_off + (uint32_t)(C::KB * kb) * (D * 2);
+#pragma unroll
+    for (int i = 0; i < C::NCH; ++i) {
+      kst[i] = load_16_stream(krs, voff, i * 1024u);
+      vst[i] = load_16_stream(vrs, voff, i * 1024u);
+    }
+  };
+  auto swrite = [&](const u32x4 (&kst)[C::NCH], const u32x4 (&vst)[C::NCH]) {
+#pragma unroll
+    for (int i = 0; i < C::NCH; ++i) {
+      const int ci = lane + 64 * i;
+      const int row = ci / C::CPR, c = ci % C::CPR;
+      *(u32x4*)(kls + row * D + 8 * dk_chunk<D>(row, c)) = kst[i];
+      *(u32x4*)(vls + row * D + 8 * dv_chunk<D>(row, c)) = vst[i];
+    }
+  };
+
+  u32x4 kA[C::NCH], vA[C::NCH], kB[C::NCH], vB[C::NCH];
+  const int kb0 = wave;
+  if (kb0 < nkb) gload(kA, vA, kb0);
+  if (kb0 + C::NW < nkb) gload(kB, vB, kb0 + C::NW);
+
+  // Qᵀ as the B operand of Sᵀ = K·Qᵀ (16x16x32): lane holds query column l16, head-dim slots
+  // 32c + 8grp .. +7.
+  u32x4 qf[D / 32];
   {
     const uint16_t* qrow = Q + (((size_t)b * Hq + hq) * Nq + qi) * D;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      qf[c] = row_ok ? *(const u32x4*)(qrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < D / 32; ++c)
+      qf[c] = row_ok ? *(const u32x4*)(qrow + 32 * c + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  const uint16_t* Kh = K + ((size_t)b * Hkv + hkv) * Nk * D;
-  const uint16_t* Vh = V + ((size_t)b * Hkv + hkv) * Nk * D;
-  uint16_t* kls = (uint16_t*)smem + wave * C::WTILE;
-  uint16_t* vls = kls + C::KB * C::KROW;
-
-  u32x4 kst[C::NCH], vst[C::NCH];
-  auto gload = [&](int kb) {
+  f32x4 oacc[D / 16];
 #pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
-      const int ci = lane + 64 * i;
-      const int row = ci / C::CPR, col = (ci % C::CPR) * 8;
-      const int key = ks0 + C::KB * kb + row;
-      if (key < ks1) {  // keys of the next split or past Nk are not this split's: zero
-        kst[i] = *(const u32x4*)(Kh + (size_t)key * D + col);
-        vst[i] = *(const u32x4*)(Vh + (size_t)key * D + col);
-      } else {
-        kst[i] = u32x4{0u, 0u, 0u, 0u};
-        vst[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto swrite = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
-      const int ci = lane + 64 * i;
-      const int row = ci / C::CPR, col = (ci % C::CPR) * 8;
-      *(u32x4*)(kls + row * C::KROW + col) = kst[i];
-      *(u32x4*)(vls + row * C::VROW + col) = vst[i];
-    }
-  };
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+  for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{};
   // m_run: the lazily moved reference the exponents use; m_true: the exact running max, which
   // the stored metadata reports
   float m_run = -INFINITY, m_true = -INFINITY, l_run = 0.f;
-  const int tr_g = lane >> 4, tr_j = (lane & 15) >> 2, tr_t = lane & 3;
+  const int tr_j = l16 >> 2, tr_t = l16 & 3;
 
-  int kb = wave;
-  if (kb < nkb) gload(kb);
-  for (; kb < nkb; kb += C::NW) {
-    swrite();
-    wave_lds_sync();
-    if (kb + C::NW < nkb) gload(kb + C::NW);  // in flight while this block is computed
+  // one staged block: scores, masked online softmax, Oᵀ += Vᵀ·Pᵀ
+  auto compute = [&](int kb) {
     const int k0 = ks0 + C::KB * kb;
-
-    f32x16 sc = f32x16{};
+    // Sᵀ (32 keys x 16 queries) in two 16-key halves: sc[h][i] is key k0 + 16h + 4grp + i
+    f32x4 sc[2];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const u32x4 a = *(const u32x4*)(kls + l32 * C::KROW + 16 * c + 8 * h);
-      sc = mfma32x32x16(a, qf[c], sc);
-    }
-    if (k0 + C::KB - 1 > lim || (CAUSAL && k0 + C::KB - 1 > off)) {
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = 16 * hh + l16;
+      sc[hh] = f32x4{};
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int key = k0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        if (key > lim) sc[rr] = -INFINITY;
+      for (int c = 0; c < D / 32; ++c) {
+        const u32x4 a = *(const u32x4*)(kls + row * D + 8 * dk_chunk<D>(row, 4 * c + grp));
+        sc[hh] = mfma16x16x32(a, qf[c], sc[hh]);
       }
     }
-    float mx = sc[0];
+    if (k0 + C::KB - 1 > lim) {
 #pragma unroll
-    for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, sc[rr]);
-    mx = pair32_max(mx);
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (k0 + 16 * hh + 4 * grp + i > lim) sc[hh][i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = quad_max(mx);
     m_true = fmaxf(m_true, mx);
     const bool grow = (mx - m_run) * scale_log2 > kLazyLog2;  // lazy reference max, as in prefill
     const float m_next = grow ? mx : m_run;
     const float alpha = grow ? fast_exp2((m_run - m_next) * scale_log2) : 1.f;
     if (wave_any(grow && m_run != -INFINITY)) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
     }
     m_run = m_next;
     const float mb = (m_run == -INFINITY ? 0.f : m_run) * scale_log2;
     float rs = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const float p = fast_exp2(fmaf(sc[rr], scale_log2, -mb));
-      sc[rr] = p;
-      rs += p;
-    }
-    l_run = l_run * alpha + rs;
-
-    u32x4 pb[2];
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const int r0 = 8 * mm;
-      pb[mm] = u32x4{pack_bf16x2(sc[r0 + 0], sc[r0 + 1]), pack_bf16x2(sc[r0 + 2], sc[r0 + 3]),
-                     pack_bf16x2(sc[r0 + 4], sc[r0 + 5]), pack_bf16x2(sc[r0 + 6], sc[r0 + 7])};
-    }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int col = 32 * db + 16 * (tr_g & 1) + 4 * tr_t;
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const int row0 = 16 * mm + 4 * h + tr_j;
-        const bf16x8 a = lds_read_tr16_pair(vls + row0 * C::VROW + col,
-                                            vls + (row0 + 8) * C::VROW + col);
-        oacc[db] = mfma32x32x16(a, pb[mm], oacc[db]);
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(fmaf(sc[hh][i], scale_log2, -mb));
+        sc[hh][i] = p;
+        rs += p;
       }
+    l_run = l_run * alpha + rs;  // this lane group's keys; the four groups are summed at the end
+    // Pᵀ (32 keys x 16 queries) as the B operand: slot 8grp + t is key 4grp + t (t < 4) or
+    // 16 + 4grp + t - 4, matching the two transposing reads below.
+    const u32x4 pb = {pack_bf16x2(sc[0][0], sc[0][1]), pack_bf16x2(sc[0][2], sc[0][3]),
+                      pack_bf16x2(sc[1][0], sc[1][1]), pack_bf16x2(sc[1][2], sc[1][3])};
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const int c = 2 * db + (tr_t >> 1), within = 4 * (tr_t & 1);
+      const int r0 = 4 * grp + tr_j, r1 = r0 + 16;
+      const bf16x8 a = lds_read_tr16_pair(vls + r0 * D + 8 * dv_chunk<D>(r0, c) + within,
+                                          vls + r1 * D + 8 * dv_chunk<D>(r1, c) + within);
+      oacc[db] = mfma16x16x32(a, pb, oacc[db]);
     }
+  };
+
+  for (int kb = kb0; kb < nkb; kb += 2 * C::NW) {
+    swrite(kA, vA);
+    wave_lds_sync();
+    if (kb + 2 * C::NW < nkb) gload(kA, vA, kb + 2 * C::NW);  // keeps two blocks in flight
+    compute(kb);
     wave_lds_sync();  // this block's LDS reads precede the next block's writes
+    if (kb + C::NW < nkb) {
+      swrite(kB, vB);
+      wave_lds_sync();
+      if (kb + 3 * C::NW < nkb) gload(kB, vB, kb + 3 * C::NW);
+      compute(kb + C::NW);
+      wave_lds_sync();
+    }
   }
 
   // merge the 4 waves' (m, l, Oᵀ) into one locally normalised partial for the split
-  const float l_tot = pair32_sum(l_run);
+  const float l_tot = quad_sum(l_run);
   __syncthreads();
-  float* ocb = (float*)smem;                // [NW][32][OROW] unnormalised Oᵀ rows
-  float* mlb = ocb + C::NW * 32 * C::OROW;  // [NW][32][3]: exact max, reference max, sum
-                                            // (score units; the sum is against the reference)
+  float* ocb = (float*)smem;                 // [NW][QC][OROW] unnormalised Oᵀ rows
+  float* mlb = ocb + C::NW * C::QC * C::OROW;  // [NW][QC][3]: exact max, reference max, sum
+                                             // (score units; the sum is against the reference)
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
-      *(f32x4*)(ocb + (wave * 32 + l32) * C::OROW + 32 * db + 8 * g4 + 4 * h) =
-          f32x4{oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2],
-                oacc[db][4 * g4 + 3]};
-  if (h == 0) {
-    mlb[(wave * 32 + l32) * 3 + 0] = m_true;
-    mlb[(wave * 32 + l32) * 3 + 1] = m_run;
-    mlb[(wave * 32 + l32) * 3 + 2] = l_tot;
+  for (int db = 0; db < D / 16; ++db)
+    *(f32x4*)(ocb + (wave * C::QC + l16) * C::OROW + 16 * db + 4 * grp) = oacc[db];
+  if (grp == 0) {
+    mlb[(wave * C::QC + l16) * 3 + 0] = m_true;
+    mlb[(wave * C::QC + l16) * 3 + 1] = m_run;
+    mlb[(wave * C::QC + l16) * 3 + 2] = l_tot;
   }
   __syncthreads();
 
-  constexpr int DE = D / 8;  // head-dim elements per thread in the merge
-  const int qr = tid >> 3, ch = tid & 7;
-  const int rr = rg * 32 + qr;
+  constexpr int TPQ = C::NT / C::QC;  // threads per query column in the merge
+  constexpr int DE = D / TPQ;         // head-dim elements per merging thread
+  const int qr = tid / TPQ, ch = tid % TPQ;
+  const int rr = rg * C::QC + qr;
   if (rr < R) {
     const int g2 = rr / Nq, qi2 = rr - g2 * Nq;
     const int hq2 = hkv * G + g2;
@@ -226,13 +258,13 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < C::NW; ++w)
-      if (mlb[(w * 32 + qr) * 3 + 2] > 0.f) M = fmaxf(M, mlb[(w * 32 + qr) * 3]);
+      if (mlb[(w * C::QC + qr) * 3 + 2] > 0.f) M = fmaxf(M, mlb[(w * C::QC + qr) * 3]);
     float ew[C::NW];
     float Lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < C::NW; ++w) {
-      const float lw = mlb[(w * 32 + qr) * 3 + 2];
-      ew[w] = lw > 0.f ? fast_exp2((mlb[(w * 32 + qr) * 3 + 1] - M) * scale_log2) : 0.f;
+      const float lw = mlb[(w * C::QC + qr) * 3 + 2];
+      ew[w] = lw > 0.f ? fast_exp2((mlb[(w * C::QC + qr) * 3 + 1] - M) * scale_log2) : 0.f;
       Lsum += ew[w] * lw;
     }
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
@@ -243,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
       f32x4 o = f32x4{};
 #pragma unroll
       for (int w = 0; w < C::NW; ++w)
-        o += ew[w] * *(const f32x4*)(ocb + (w * 32 + qr) * C::OROW + ch * DE + e);
+        o += ew[w] * *(const f32x4*)(ocb + (w * C::QC + qr) * C::OROW + ch * DE + e);
       *(f32x4*)(dst + e) = o * inv;
     }
     if (ch == 0) {
@@ -265,9 +297,10 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wave per output row (batch, query head, position).  Lane s reads the metadata of split s
-// (64 splits per pass), so all metadata loads are in flight together; the weights
-// w_s = l_s exp(m_s - M) are then broadcast lane by lane while the partial rows stream in.
+// One wave per output row (batch, query head, position).  The first 16 partial rows are
+// requested before anything else, so their latency overlaps the metadata pass; lane s reads the
+// (m, l) of split s (64 splits per pass), the weights w_s = l_s exp(m_s - M) are then broadcast
+// lane by lane, and the rows are accumulated in split order (deterministic).
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ wsO,
                                                            const float* __restrict__ wsML,
@@ -275,37 +308,45 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
                                                            float* __restrict__ LSE, int rows,
                                                            int S) {
   constexpr int E = D / 64;  // head-dim elements per lane
+  constexpr int CH = 16;     // partial rows in flight per lane
+  typedef float vecE __attribute__((ext_vector_type(E)));
   const int lane = threadIdx.x;
   const int row = blockIdx.x;
   if (row >= rows) return;
   const f32x2* ml = (const f32x2*)(wsML + (size_t)row * S * 2);
-  float M = -INFINITY;
+  const float* src = wsO + (size_t)row * S * D + lane * E;
+
+  vecE o[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) o[j] = (j < S) ? *(const vecE*)(src + (size_t)j * D) : vecE{};
+
+  float M = -INFINITY;  // exact max over the splits that saw a key
   for (int s0 = 0; s0 < S; s0 += 64) {
     const f32x2 v = (s0 + lane < S) ? ml[s0 + lane] : f32x2{-INFINITY, 0.f};
     M = fmaxf(M, v[1] > 0.f ? v[0] : -INFINITY);
   }
   M = wave_max(M);
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+
+  vecE acc = vecE{};
   float W = 0.f;
-  const float* src = wsO + (size_t)row * S * D + lane * E;
   for (int s0 = 0; s0 < S; s0 += 64) {
     const int n = min(64, S - s0);
     const f32x2 v = (lane < n) ? ml[s0 + lane] : f32x2{-INFINITY, 0.f};
     const float w = v[1] > 0.f ? v[1] * fast_exp2((v[0] - M) * kLog2e) : 0.f;
     W += w;
-#pragma unroll 8
-    for (int j = 0; j < n; ++j) {
-      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                     __builtin_bit_cast(int, w), j));
-      const float* p = src + (size_t)(s0 + j) * D;
-      if constexpr (E == 2) {
-        const f32x2 o = *(const f32x2*)p;
-        acc[0] = fmaf(wj, o[0], acc[0]);
-        acc[1] = fmaf(wj, o[1], acc[1]);
-      } else {
-        acc[0] = fmaf(wj, p[0], acc[0]);
+    for (int c0 = 0; c0 < n; c0 += CH) {
+      if (s0 + c0 > 0) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          o[j] = (c0 + j < n) ? *(const vecE*)(src + (size_t)(s0 + c0 + j) * D) : vecE{};
+      }
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        if (c0 + j < n) {
+          const float wj = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), c0 + j));
+          acc += wj * o[j];
+        }
       }
     }
   }
@@ -327,7 +368,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, float*
   using C = DecCfg<D>;
   const int L = (sh.Nk + S - 1) / S;
   const int R = (sh.Hq / sh.Hkv) * sh.Nq;
-  const int nrg = (R + 31) / 32;
+  const int nrg = (R + C::QC - 1) / C::QC;
   const long long blocks = (long long)sh.B * sh.Hkv * nrg * S;
   const long long rows = (long long)sh.B * sh.Hq * sh.Nq;
   if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;

