@@ -173,3 +173,38 @@ def attn_decode_splitkv(q, k, v, n_splits: int, causal: bool = True, scale: floa
                                     int(n_splits), _stream(q.device))
     _check_rc(rc, "attn_decode_splitkv")
     return out, lse, workspace
+
+
+def prepare_fwd(q, k, v, out, lse=None, causal: bool = True, scale: float = 0.0):
+    """A zero-argument callable that enqueues ``attn_fwd`` with these tensors on the current
+    stream, with every argument marshalled once up front (for timing loops)."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    fn = load().attn_fwd
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, float(scale),
+            int(bool(causal)), _stream(q.device))
+
+    def call():
+        rc = fn(*args)
+        if rc != ATTN_OK:
+            _check_rc(rc, "attn_fwd")
+    return call
+
+
+def prepare_decode(q, k, v, n_splits: int, out, lse, workspace, causal: bool = True,
+                   scale: float = 0.0):
+    """The same for ``attn_decode_splitkv``."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    fn = load().attn_decode_splitkv
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+            int(bool(causal)), int(n_splits), _stream(q.device))
+
+    def call():
+        rc = fn(*args)
+        if rc != ATTN_OK:
+            _check_rc(rc, "attn_decode_splitkv")
+    return call
