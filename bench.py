@@ -8,9 +8,11 @@ in HBM:
              d=128, n_splits=16, once with Nq=1 and once with Nq=4.  Four distinct K/V buffer sets
              (4 x 268 MB) are rotated so the 256 MB MALL cannot serve repeated reads.
 
-Every kernel launch of the timed region is bracketed by HIP events recorded on the stream the
-library launches on (torch's current stream); the calls are marshalled once before the timed
-region so that host-side overhead cannot leave the GPU idle inside a bracket.  The printed JSON line carries:
+The timed region runs exactly K steps, grouped by part: the K prefill launches back to back, then
+the K decode (Nq=1) calls, then the K decode (Nq=4) calls, each group between one pair of HIP
+events recorded on the stream the library launches on (torch's current stream).  Per-launch event
+pairs were avoided because each adds about 5 us of marker overhead.  The calls are marshalled once
+before the timed region so that host-side overhead cannot leave the GPU idle inside a bracket.  The printed JSON line carries:
   value      prefill TFLOPS (4*B*H*N^2*d / 2 for causal, over the prefill kernel's mean time);
   decode     HBM GB/s of the split + combine pair over the algorithmic bytes (K and V once, Q, O,
              LSE), for Nq=1 and Nq=4;
@@ -132,25 +134,27 @@ def decode_kv_sets(torch, I, w, n):
 
 
 def time_steps(torch, parts, steps, warmup):
-    """Run warmup untimed steps, then exactly `steps` steps; each part of each step is bracketed
-    by events on the current stream.  Returns (wall ms per step, [mean ms per part])."""
+    """Run warmup untimed steps, then exactly `steps` steps.  The timed region is grouped by part:
+    part j runs its `steps` launches back to back between one pair of events on the current
+    stream, then part j+1 follows.  (An event pair around every single launch adds about 5 us of
+    marker overhead per bracket on this stack, which would inflate each kernel's time.)
+    Returns (wall ms per step, [mean ms per launch of each part])."""
     for i in range(warmup):
         for p in parts:
             p(i)
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in parts] for _ in range(steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in parts]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        for j, p in enumerate(parts):
-            ev[i][j][0].record()
+    for j, p in enumerate(parts):
+        ev[j][0].record()
+        for i in range(steps):
             p(i)
-            ev[i][j][1].record()
+        ev[j][1].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    means = [sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)) / steps
-             for j in range(len(parts))]
+    means = [ev[j][0].elapsed_time(ev[j][1]) / steps for j in range(len(parts))]
     return wall_ms, means
 
 

@@ -89,12 +89,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-// 16 bytes per lane from `rsrc` at byte offset `voff` straight into LDS: lane i's bytes land at
-// `lds_base` + 16 i (`lds_base` must be the same for the whole wave).
+// 16 bytes per lane from `rsrc` at byte offset voff + soff straight into LDS: lane i's bytes
+// land at `lds_base` + 16 i (`lds_base` and `soff` must be the same for the whole wave).  Both
+// offsets take part in the range check.  The instruction's immediate offset field is left at
+// zero on purpose: it would also move the LDS destination (measured on gfx950).
 __device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t rsrc, void* lds_base,
-                                            uint32_t voff) {
+                                            uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, 0, 0, 0);
+      rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, (int)soff, 0, 0);
 }
 
 // 16 bytes per lane from `rsrc` at byte offset voff + soff into registers (zero past the end),

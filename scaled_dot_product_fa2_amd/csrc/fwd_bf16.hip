@@ -16,20 +16,33 @@
 //     plus one permlane32 swap with lane l^32.
 //   * Oᵀ += Vᵀ·Pᵀ on the same MFMA: Pᵀ is the B operand straight from the score registers (packed
 //     to bf16); the matching key order of Vᵀ comes from the transposing LDS read ds_read_b64_tr_b16,
-//     so V stays row-major in LDS.  Every Oᵀ accumulator of a lane belongs to its own query, so the
-//     rescale by exp2((m_old - m_new)·scale·log2e) is a per-lane scalar multiply, and it is only
-//     done when some row's max grew by more than 2^8 (lazy rescaling; O and l keep one reference).
+//     so V stays row-major in LDS.  Every Oᵀ accumulator of a lane belongs to its own query, so a
+//     rescale is a per-lane scalar multiply.
+//   * Lazy rescaling: exponents are taken against a reference max that only moves when a block
+//     holds a score more than 2^8 above it (in exp2 units), so probabilities stay below 2^8 and O
+//     and l, which share the reference, are rarely rescaled.  The common case needs no block max:
+//     the max of the exponent arguments is checked after the fact, and the rare block that
+//     exceeds the bound is redone against its own max (scores recomputed from global K).
+//   * Software pipelining: in steady state a step exponentiates block t while issuing block
+//     t+1's QK products, instruction by instruction (scheduling fences keep the order), and then
+//     issues block t's PV products 16 keys at a time while the next 16 keys are exponentiated.
+//     The matrix cores therefore run while the transcendental and VALU work issues.  Blocks that
+//     need a mask (the causal diagonal, a ragged end) run an unpipelined step instead.
 //   * K/V blocks go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane, no
-//     register staging), double buffered: the next block's loads are issued right after the
-//     barrier that publishes the current one.  Rows past the end of K/V read as zero through the
-//     buffer range check.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled, K and
-//     V each with the swizzle that makes its read pattern conflict-free on the 64 LDS banks.
+//     register staging).  K runs one block ahead of V: at the start of step t, K[t+1] and V[t]
+//     are in LDS and K[t+2], V[t+1] are requested, so two buffers each suffice; every buffer is
+//     its own LDS variable so the compiler can tell the in-flight copies from the reads.  Rows
+//     past the end of K/V read as zero through the buffer range check.  Rows are stored unpadded
+//     with their 16-byte chunks XOR-swizzled, K and V each with the swizzle that makes its read
+//     pattern conflict-free on the 64 LDS banks.
 //   * Workgroups are ordered heaviest-first under the causal mask, and all query blocks of one
 //     (batch, head) are kept on one XCD so their shared K/V stays in that XCD's L2.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -41,7 +54,6 @@ struct FwdCfg {
   static constexpr int NT = 256;                     // threads per workgroup (4 waves)
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int TILE = BC * D;                // bf16 elements per K or V block
-  static constexpr int STAGE = 2 * TILE;             // one K block + one V block
   static constexpr int RPL = 64 / CPR;               // rows covered by one wave-wide 1 KB load
   static constexpr int LPW = BC / RPL / 4;           // 1 KB loads per wave per tensor per block
   static_assert(BC % (4 * RPL) == 0, "staging must divide evenly");
@@ -88,7 +100,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq,
     int Hkv, int Nq, int Nk, int nqt, float scale, float scale_log2) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::STAGE];
+  constexpr int NC = D / 16;  // 16-element head-dim slices per QK product
+  __shared__ __attribute__((aligned(1024))) uint16_t kl0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kl1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vl0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vl1[C::TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -104,35 +120,53 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int my_q = qw0 + l32;
 
   const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + (size_t)(b * Hkv + hkv) * Nk * D, kv_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + (size_t)(b * Hkv + hkv) * Nk * D, kv_bytes);
+  const uint16_t* kg = K + (size_t)(b * Hkv + hkv) * Nk * D;
+  const uint16_t* vg = V + (size_t)(b * Hkv + hkv) * Nk * D;
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(Nq - 1, q_tile0 + C::BR - 1) + off + 1);
   const int n_tiles = kv_end > 0 ? (kv_end + C::BC - 1) / C::BC : 0;
 
-  // Qᵀ as the MFMA B operand: lane holds query my_q, head-dim slots 16c + 8h .. +7.
-  u32x4 qf[D / 16];
+  u32x4 qf[NC];
   {
     const uint16_t* qrow = Q + ((size_t)bh * Nq + my_q) * D;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
+    for (int c = 0; c < NC; ++c)
       qf[c] = (my_q < Nq) ? *(const u32x4*)(qrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  // This lane's slot in the wave's 1 KB direct loads: row within the load, physical chunk.
+  // Direct loads: the buffer resource of block t starts at that block and covers the rest of K
+  // (or V), so a lane's offset is the same for every block; rows past Nk read as zero.  Load i
+  // of a wave fills rows (4i + wave)·RPL .. +RPL-1, which keeps each lane's swizzled chunk the
+  // same for every i: the i-dependent part is a plain byte offset, passed as the scalar offset.
   const int ld_row = lane / C::CPR, ld_chunk = lane % C::CPR;
-  auto issue_loads = [&](int t, int buf) {
-    uint16_t* kbase = smem + buf * C::STAGE;
-    uint16_t* vbase = kbase + C::TILE;
+  const int row0 = wave * C::RPL + ld_row;
+  const uint32_t koff = (uint32_t)row0 * (D * 2) + 16u * k_chunk<D>(row0, ld_chunk);
+  const uint32_t voff = (uint32_t)row0 * (D * 2) + 16u * v_chunk<D>(row0, ld_chunk);
+  auto issue = [&](const uint16_t* g, int t, uint16_t* dst, uint32_t lane_off) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(g + (size_t)t * C::BC * D, kv_bytes - (uint32_t)t * (C::BC * D * 2));
 #pragma unroll
-    for (int i = 0; i < C::LPW; ++i) {
-      const int blk = wave * C::LPW + i;  // which 1 KB piece of the block
-      const int row = blk * C::RPL + ld_row;
-      const uint32_t rowoff = (uint32_t)(t * C::BC + row) * (D * 2);
-      load_lds_16(krs, kbase + blk * 512, rowoff + 16u * k_chunk<D>(row, ld_chunk));
-      load_lds_16(vrs, vbase + blk * 512, rowoff + 16u * v_chunk<D>(row, ld_chunk));
-    }
+    for (int i = 0; i < C::LPW; ++i)
+      load_lds_16(rs, dst + (4 * i + wave) * 512, lane_off, (uint32_t)i * (4 * C::RPL * D * 2));
+  };
+  auto issue_k = [&](int t, uint16_t* dst) { issue(kg, t, dst, koff); };
+  auto issue_v = [&](int t, uint16_t* dst) { issue(vg, t, dst, voff); };
+
+  // LDS read addresses.  Rows start on 256-byte (D = 128) or 128-byte (D = 64) boundaries and
+  // every swizzle XORs the logical chunk index with a function of the row, so the address of
+  // logical chunk c is this lane's address of chunk 0 XOR (16 c): one VALU op per read.
+  const uint32_t k_lane = (uint32_t)(l32 * D + 8 * k_chunk<D>(l32, h)) * 2;
+  const int tr_g = lane >> 4, tr_j = (lane & 15) >> 2, tr_t = lane & 3;
+  const int v_r0 = 4 * h + tr_j;
+  const uint32_t v_lane =
+      (uint32_t)(v_r0 * D + 8 * v_chunk<D>(v_r0, 2 * (tr_g & 1) + (tr_t >> 1)) + 4 * (tr_t & 1)) * 2;
+  // byte address of K operand (kb, c) / V operand base for head-dim block db, within a buffer
+  auto k_addr = [&](const uint16_t* buf, int c) {
+    return (const u32x4*)((const char*)buf + (k_lane ^ (32u * c)));
+  };
+  auto v_addr = [&](const uint16_t* buf, int db) {
+    return (const uint16_t*)((const char*)buf + (v_lane ^ (64u * db)));
   };
 
   f32x16 oacc[D / 32];
@@ -140,107 +174,284 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // transposing-read coordinates of this lane (see the layout note in fa_device.h)
-  const int tr_g = lane >> 4, tr_j = (lane & 15) >> 2, tr_t = lane & 3;
+  auto active = [&](int t) { return (qw0 < Nq) && (!CAUSAL || t * C::BC <= qw0 + 31 + off); };
 
-  if (n_tiles > 0) issue_loads(0, 0);
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    wait_vmem();       // this wave's share of block t has landed in LDS
-    __syncthreads();   // ... and everyone's; everyone is also done reading the other buffer
-    if (t + 1 < n_tiles) issue_loads(t + 1, buf ^ 1);
-    const uint16_t* ks = smem + buf * C::STAGE;
-    const uint16_t* vs = ks + C::TILE;
-    const int k0 = t * C::BC;
-    const bool active = (qw0 < Nq) && (!CAUSAL || k0 <= qw0 + 31 + off);
-    if (active) {
-      // Sᵀ = K·Qᵀ for two 32-key halves of the block; all K operands are read up front
-      u32x4 kop[2][D / 16];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = 32 * kb + l32;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-          kop[kb][c] = *(const u32x4*)(ks + row * D + 8 * k_chunk<D>(row, 2 * c + h));
-      }
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) s[kb] = mfma32x32x16(kop[kb][c], qf[c], s[kb]);
-      }
-      // mask keys past Nk and, on diagonal blocks, keys after this row's last visible key
-      const bool need_mask = (k0 + C::BC > Nk) || (CAUSAL && (k0 + C::BC - 1 > qw0 + off));
-      if (need_mask) {
-        const int lim = CAUSAL ? min(Nk - 1, my_q + off) : Nk - 1;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > lim) s[kb][r] = -INFINITY;
-          }
-      }
-      // online softmax (per lane = per query): block max, lazily moved reference max, rescale,
-      // exponentiate, running sum
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = pair32_max(mx);
-      const bool grow = (mx - m_run) * scale_log2 > kLazyLog2;  // false while both are -inf
-      const float m_next = grow ? mx : m_run;
-      const float alpha = grow ? fast_exp2((m_run - m_next) * scale_log2) : 1.f;
-      if (wave_any(grow && m_run != -INFINITY)) {  // an already-started row moves its max
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-      }
-      m_run = m_next;
-      const float mb = (m_run == -INFINITY ? 0.f : m_run) * scale_log2;
-      float rs = 0.f;
+  // keys past Nk and, on diagonal blocks, keys after this row's last visible key -> -inf
+  auto mask = [&](int k0, f32x16 (&s)[2]) {
+    const bool need = (k0 + C::BC > Nk) || (CAUSAL && (k0 + C::BC - 1 > qw0 + off));
+    if (need) {
+      const int lim = CAUSAL ? min(Nk - 1, my_q + off) : Nk - 1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -mb));
-          s[kb][r] = p;
-          rs += p;
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key > lim) s[kb][r] = -INFINITY;
         }
-      l_run = l_run * alpha + rs;  // lane-half partial; the partner half is added at the end
+    }
+  };
 
-      // Pᵀ as B operands: block kb, 16-key group mm uses score registers 8mm .. 8mm+7
-      u32x4 pb[4];
+  // Sᵀ = K·Qᵀ of one block from LDS, K operands read one slice ahead
+  auto scores_lds = [&](const uint16_t* ks, f32x16 (&s)[2]) {
+    u32x4 ka0 = *k_addr(ks, 0);
+    u32x4 ka1 = *(k_addr(ks, 0) + 32 * D / 8);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int c = 0; c < NC; ++c) {
+      u32x4 kn0 = ka0, kn1 = ka1;
+      if (c + 1 < NC) {
+        kn0 = *k_addr(ks, c + 1);
+        kn1 = *(k_addr(ks, c + 1) + 32 * D / 8);
+      }
+      s[0] = mfma32x32x16(ka0, qf[c], s[0]);
+      s[1] = mfma32x32x16(ka1, qf[c], s[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      ka0 = kn0;
+      ka1 = kn1;
+    }
+  };
+
+  // The same straight from global memory (the rarely taken path that redoes a block), two
+  // operands at a time
+  auto scores_global = [&](int k0, f32x16 (&s)[2]) {
+    const int row0 = k0 + l32, row1 = row0 + 32;
+    const uint16_t* kr0 = kg + (size_t)min(row0, Nk - 1) * D + 8 * h;
+    const uint16_t* kr1 = kg + (size_t)min(row1, Nk - 1) * D + 8 * h;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const int r0 = 8 * mm;
-          pb[2 * kb + mm] = u32x4{pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]),
-                                  pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]),
-                                  pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]),
-                                  pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7])};
+    for (int c = 0; c < NC; ++c) {
+      const u32x4 a0 = row0 < Nk ? *(const u32x4*)(kr0 + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 a1 = row1 < Nk ? *(const u32x4*)(kr1 + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+      s[0] = mfma32x32x16(a0, qf[c], s[0]);
+      s[1] = mfma32x32x16(a1, qf[c], s[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // exponent arguments x = s·scale·log2e - mb of score pair (j, j+1), in place, and their max
+  auto arg_pair = [&](f32x16 (&s)[2], float& amax, float mb, int j) {
+    const int kb = j >> 4, r = j & 15;
+    const float x0 = fmaf(s[kb][r], scale_log2, -mb);
+    const float x1 = fmaf(s[kb][r + 1], scale_log2, -mb);
+    amax = fmaxf(amax, fmaxf(x0, x1));
+    s[kb][r] = x0;
+    s[kb][r + 1] = x1;
+    asm volatile("" ::"v"(x0), "v"(x1));  // keeps this work here, between the matrix products
+  };
+  // probabilities 2^x of pair (j, j+1), in place, packed into P
+  auto exp_pair = [&](f32x16 (&s)[2], u32x4 (&pb)[4], int j) {
+    const int kb = j >> 4, r = j & 15;
+    const float p0 = fast_exp2(s[kb][r]), p1 = fast_exp2(s[kb][r + 1]);
+    s[kb][r] = p0;
+    s[kb][r + 1] = p1;
+    const uint32_t pk = pack_bf16x2(p0, p1);
+    asm volatile("" ::"v"(pk));
+    pb[j >> 3][(j >> 1) & 3] = pk;
+  };
+
+  // The block's exact max becomes the reference: rescale O and l, recompute the arguments and
+  // group 0's probabilities (only for blocks that need no mask).
+  auto redo_block = [&](f32x16 (&s)[2], u32x4 (&pb)[4], int k0, float& mb) {
+    scores_global(k0, s);
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = pair32_max(mx);
+    const float m_next = fmaxf(m_run, mx);
+    const float alpha = m_next == -INFINITY ? 1.f : fast_exp2((m_run - m_next) * scale_log2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    l_run *= alpha;
+    m_run = m_next;
+    mb = (m_run == -INFINITY ? 0.f : m_run) * scale_log2;
+    float amax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) arg_pair(s, amax, mb, j);
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) exp_pair(s, pb, j);
+  };
+
+  f32x16 sA[2], sB[2];
+
+  // Blocks [0, n_free) need no mask for any wave of the workgroup: every key is below Nk and,
+  // under the causal mask, visible to the workgroup's first query row.
+  int n_free = Nk / C::BC;
+  if (CAUSAL) n_free = min(n_free, max(0, (q_tile0 + off + 1) / C::BC));
+  n_free = min(n_free, n_tiles);
+
+  // Steady-state step for an unmasked block t (scores in `s`): block t's exponentials are
+  // interleaved instruction by instruction with the QK products of block t+1 (into `sn`), so
+  // the transcendental and VALU work issues while the matrix cores run; then Oᵀ += Vᵀ·Pᵀ for
+  // block t, interleaved with the row sums.  Buffers: K[t] and V[t] live in kl/vl[t % 2]; at
+  // the start of step t, K[t+1] and V[t] have landed, and K[t+2] and V[t+1] are requested.
+  auto step = [&](int t, auto bufc, f32x16 (&s)[2], f32x16 (&sn)[2]) {
+    constexpr int BUF = decltype(bufc)::value;
+    uint16_t* const k_next = BUF ? kl0 : kl1;   // block t+1's keys
+    uint16_t* const k_free = BUF ? kl1 : kl0;   // block t's keys, no longer read
+    uint16_t* const v_cur = BUF ? vl1 : vl0;    // block t's values
+    uint16_t* const v_next = BUF ? vl0 : vl1;
+    wait_vmem();       // this wave's loads of K[t+1] and V[t] have landed ...
+    __syncthreads();   // ... and everyone's; K[t] and V[t-1] are free again
+    if (t + 2 < n_tiles) issue_k(t + 2, k_free);
+    if (t + 1 < n_tiles) issue_v(t + 1, v_next);
+    if (qw0 >= Nq) return;
+    // Block t+1's products are always issued (when t+1 does not exist or is inactive for this
+    // wave, they read whatever the buffer holds and the result is never used).  Interleaved with
+    // them: block t's exponent arguments and max, and at the end group 0's probabilities.
+    float mb = m_run * scale_log2;
+    float amax = -INFINITY;
+    u32x4 pb[4];
+    constexpr int NS = 2 * NC;            // products in this part
+    constexpr int APS = 32 / NS;          // arguments per product
+    constexpr int G0 = NS - 4;            // first product that also takes group 0's exponentials
+    {
+      u32x4 kr[3][2];
+      kr[0][0] = *k_addr(k_next, 0);
+      kr[0][1] = *(k_addr(k_next, 0) + 32 * D / 8);
+      kr[1][0] = *k_addr(k_next, 1);
+      kr[1][1] = *(k_addr(k_next, 1) + 32 * D / 8);
+      sn[0] = f32x16{};
+      sn[1] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c + 2 < NC) {
+          kr[(c + 2) % 3][0] = *k_addr(k_next, c + 2);
+          kr[(c + 2) % 3][1] = *(k_addr(k_next, c + 2) + 32 * D / 8);
         }
-      // Oᵀ += Vᵀ·Pᵀ.  Operand slot 8h + 4c + j of group (kb, mm) holds key
-      // 32kb + 16mm + 8c + 4h + j, matching the score register order above.
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int chunk = 4 * db + 2 * (tr_g & 1) + (tr_t >> 1);
-        const int within = 4 * (tr_t & 1);
-        bf16x8 vop[4];
+        for (int hh = 0; hh < 2; ++hh) {
+          const int slot = 2 * c + hh;
+          sn[hh] = mfma32x32x16(kr[c % 3][hh], qf[c], sn[hh]);
 #pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-          const int r0 = 16 * m4 + 4 * h + tr_j, r1 = r0 + 8;
-          vop[m4] = lds_read_tr16_pair(vs + r0 * D + 8 * v_chunk<D>(r0, chunk) + within,
-                                       vs + r1 * D + 8 * v_chunk<D>(r1, chunk) + within);
+          for (int j = slot * APS; j < (slot + 1) * APS; j += 2) arg_pair(s, amax, mb, j);
+          if (slot >= G0) exp_pair(s, pb, 2 * (slot - G0));
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
+    }
+    // an argument above kLazyLog2, or no reference yet: redo the block against its max
+    if (wave_any(!(amax <= kLazyLog2) || m_run == -INFINITY)) redo_block(s, pb, t * C::BC, mb);
+
+    // Oᵀ += Vᵀ·Pᵀ, 16-key group by group (group g is operand pb[g]); while group g's products
+    // run, group g+1's exponentials and group g's row sums are done.  V operands of group g+1
+    // are read while group g's products run.
+    constexpr int NDB = D / 32;
+    float rs = 0.f;
+    bf16x8 vop[2][NDB];
 #pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) oacc[db] = mfma32x32x16(vop[m4], pb[m4], oacc[db]);
+    for (int db = 0; db < NDB; ++db)
+      vop[0][db] = lds_read_tr16_pair(v_addr(v_cur, db), v_addr(v_cur, db) + 8 * D);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        if (g + 1 < 4)
+          vop[(g + 1) & 1][db] = lds_read_tr16_pair(v_addr(v_cur, db) + 16 * (g + 1) * D,
+                                                    v_addr(v_cur, db) + (16 * (g + 1) + 8) * D);
+        oacc[db] = mfma32x32x16(vop[g & 1][db], pb[g], oacc[db]);
+        // group g+1's exponentials: 8 values over this group's NDB products
+#pragma unroll
+        for (int j = 8 * (g + 1) + db * 8 / NDB; j < 8 * (g + 1) + (db + 1) * 8 / NDB; j += 2)
+          if (g + 1 < 4) exp_pair(s, pb, j);
+        // group g's row sums
+#pragma unroll
+        for (int j = 8 * g + db * 8 / NDB; j < 8 * g + (db + 1) * 8 / NDB; ++j)
+          rs += s[j >> 4][j & 15];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    l_run += rs;  // lane-half partial; the partner half is added at the end
+  };
+
+  // Step for a block that may need masking (diagonal or ragged end), done in order: mask,
+  // exact block max and lazy rescale, exponentials, PV, then block t+1's scores.  Same buffers.
+  auto step_tail = [&](int t, f32x16 (&s)[2]) {
+    const int k0 = t * C::BC;
+    uint16_t* const k_next = (t & 1) ? kl0 : kl1;
+    uint16_t* const k_free = (t & 1) ? kl1 : kl0;
+    const uint16_t* const v_cur = (t & 1) ? vl1 : vl0;
+    uint16_t* const v_next = (t & 1) ? vl0 : vl1;
+    wait_vmem();
+    __syncthreads();
+    if (t + 2 < n_tiles) issue_k(t + 2, k_free);
+    if (t + 1 < n_tiles) issue_v(t + 1, v_next);
+    if (!active(t)) return;
+    mask(k0, s);
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = pair32_max(mx);
+    const bool grow = (mx - m_run) * scale_log2 > kLazyLog2;  // false while both are -inf
+    const float m_next = grow ? mx : m_run;
+    const float alpha = grow ? fast_exp2((m_run - m_next) * scale_log2) : 1.f;
+    if (wave_any(grow && m_run != -INFINITY)) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    }
+    m_run = m_next;
+    const float mb = (m_run == -INFINITY ? 0.f : m_run) * scale_log2;
+    float rs = 0.f, amax = -INFINITY;
+    u32x4 pb[4];
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) arg_pair(s, amax, mb, j);
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) exp_pair(s, pb, j);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rs += s[kb][r];
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      bf16x8 vop[4];
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4)
+        vop[m4] = lds_read_tr16_pair(v_addr(v_cur, db) + 16 * m4 * D,
+                                     v_addr(v_cur, db) + (16 * m4 + 8) * D);
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) oacc[db] = mfma32x32x16(vop[m4], pb[m4], oacc[db]);
+    }
+    if (t + 1 < n_tiles && active(t + 1)) scores_lds(k_next, s);
+  };
+
+  // prologue: K[0] in, then block 0's scores; when block 0 is unmasked its exact max becomes
+  // the first reference
+  if (n_tiles > 0) {
+    issue_k(0, kl0);
+    wait_vmem();
+    __syncthreads();
+    if (n_tiles > 1) issue_k(1, kl1);
+    issue_v(0, vl0);
+    if (active(0)) {
+      scores_lds(kl0, sA);
+      if (n_free > 0) {
+        float mx = sA[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sA[kb][r]);
+        m_run = pair32_max(mx);
       }
     }
   }
+  int t = 0;
+  for (; t + 1 < n_free; t += 2) {
+    step(t, std::integral_constant<int, 0>{}, sA, sB);
+    step(t + 1, std::integral_constant<int, 1>{}, sB, sA);
+  }
+  if (t < n_free) {
+    step(t, std::integral_constant<int, 0>{}, sA, sB);
+    ++t;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sA[kb] = sB[kb];
+  }
+  for (; t < n_tiles; ++t) step_tail(t, sA);
 
   // epilogue: one 1/l per row, bf16 output, natural-log logsumexp
   const float l_tot = pair32_sum(l_run);
