@@ -144,8 +144,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const uint32_t koff = (uint32_t)row0 * (D * 2) + 16u * k_chunk<D>(row0, ld_chunk);
   const uint32_t voff = (uint32_t)row0 * (D * 2) + 16u * v_chunk<D>(row0, ld_chunk);
   auto issue = [&](const uint16_t* g, int t, uint16_t* dst, uint32_t lane_off) {
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(g + (size_t)t * C::BC * D, kv_bytes - (uint32_t)t * (C::BC * D * 2));
+    // a block at or past the end gets an empty resource: every lane reads zero
+    const uint32_t skip = (uint32_t)min(t * C::BC, Nk) * (D * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(g + (size_t)skip / 2, kv_bytes - skip);
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i)
       load_lds_16(rs, dst + (4 * i + wave) * 512, lane_off, (uint32_t)i * (4 * C::RPL * D * 2));
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     wait_vmem();       // this wave's loads of K[t+1] and V[t] have landed ...
     __syncthreads();   // ... and everyone's; K[t] and V[t-1] are free again
     if (t + 2 < n_tiles) issue_k(t + 2, k_free);
-    if (t + 1 < n_tiles) issue_v(t + 1, v_next);
+    if (t + 1 < n_tiles && t >= 1) issue_v(t + 1, v_next);  // V[1] came with the prologue
     if (qw0 >= Nq) return;
     // Block t+1's products are always issued (when t+1 does not exist or is inactive for this
     // wave, they read whatever the buffer holds and the result is never used).  Interleaved with
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     wait_vmem();
     __syncthreads();
     if (t + 2 < n_tiles) issue_k(t + 2, k_free);
-    if (t + 1 < n_tiles) issue_v(t + 1, v_next);
+    if (t + 1 < n_tiles && t >= 1) issue_v(t + 1, v_next);  // V[1] came with the prologue
     if (!active(t)) return;
     mask(k0, s);
     float mx = s[0][0];
@@ -420,14 +421,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     if (t + 1 < n_tiles && active(t + 1)) scores_lds(k_next, s);
   };
 
-  // prologue: K[0] in, then block 0's scores; when block 0 is unmasked its exact max becomes
-  // the first reference
+  // prologue: K[0], V[0], K[1], V[1] are requested together (all four buffers are free), the
+  // wave waits for K[0] only, then block 0's scores; when block 0 is unmasked its exact max
+  // becomes the first reference.  Loads complete in issue order, so "at most 3·LPW loads
+  // outstanding" means K[0] (and the Q rows loaded before it) have landed.
   if (n_tiles > 0) {
     issue_k(0, kl0);
-    wait_vmem();
-    __syncthreads();
-    if (n_tiles > 1) issue_k(1, kl1);
     issue_v(0, vl0);
+    issue_k(1, kl1);
+    issue_v(1, vl1);
+    constexpr int later = 3 * C::LPW;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (later & 15) | ((later >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // every wave's share of K[0] is in LDS
+    asm volatile("" ::: "memory");
     if (active(0)) {
       scores_lds(kl0, sA);
       if (n_free > 0) {
