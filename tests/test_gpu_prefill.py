@@ -85,7 +85,8 @@ def test_config_long_causal_b1h8n16384_sampled():
 
 
 # (B, Hq, Hkv, Nq, Nk, d, causal): ragged tails, one-row and one-key problems, Nq != Nk in both
-# directions (Nq > Nk leaves the first rows with no visible key), GQA, head dim 64.
+# directions (Nq > Nk leaves the first rows with no visible key), GQA, head dim 64, and grids of
+# one and of several rounds of workgroups.
 EDGE_CASES = [
     (1, 2, 2, 1, 1, 128, True),
     (1, 2, 2, 77, 77, 128, True),
@@ -97,6 +98,9 @@ EDGE_CASES = [
     (3, 2, 2, 130, 70, 128, False),
     (1, 2, 2, 65, 63, 64, True),
     (2, 16, 4, 384, 384, 128, False),
+    # grids of more than 512 workgroups (more than one round of two per CU), full-tensor
+    (4, 64, 16, 300, 300, 64, True),
+    (4, 64, 64, 200, 333, 128, False),
 ]
 
 
