@@ -24,6 +24,15 @@ Readings where the pages are silent (each applied identically everywhere):
 * Logsumexp is the natural log of the sum of exp over the scaled, masked scores of a row.
 * GQA: query head hq reads K/V head hq // (Hq / Hkv).
 * Splits are contiguous key chunks of ceil(Nk / n_splits) keys; the last ones may be short/empty.
+* Variable key lengths (``seqlens_k``, the "가변 시퀀스 길이" of the onnxruntime page, whose decode
+  kernel reads the KV length on the GPU): ``seqlens_k[b]`` is the number of valid keys of batch
+  element b (0 <= L_b <= Nk, the capacity of the K/V tensors).  Keys at or past L_b do not exist
+  for that element, and causal visibility uses its own length: j <= i + (L_b - Nq).  Split
+  chunks stay those of the capacity Nk, clipped to L_b.
+* Attention bias (the same page, section "1. 커널 퓨전": the fused decode kernel applies the
+  attention bias and the causal mask after QKᵀ, with bias dimensions 0 and 1 broadcast): a
+  tensor [Bb, Hb, Nq, Nk] with Bb in {1, B} and Hb in {1, Hq} is added to the scaled scores
+  before masking: s = scale·q·kᵀ + bias.
 
 All arithmetic is numpy float64; the matrix product (``@``) is the only library primitive.
 """
@@ -98,11 +107,39 @@ def _resolve_scale(scale: float, d: int) -> float:
     return 1.0 / math.sqrt(d) if scale == 0 else float(scale)
 
 
-def attention_fp64(q, k, v, scale: float, causal: bool, row_block: int = 1024
-                   ) -> Tuple[np.ndarray, np.ndarray]:
-    """O [B,Hq,Nq,d] and LSE [B,Hq,Nq] of softmax(scale·q·kᵀ + causal mask)·v, in fp64.
+def _key_lengths(seqlens_k, B: int, Nk: int) -> np.ndarray:
+    """Valid keys per batch element: all Nk, or ``seqlens_k[b]`` (checked to lie in [0, Nk])."""
+    if seqlens_k is None:
+        return np.full(B, Nk, dtype=np.int64)
+    L = np.asarray(seqlens_k, dtype=np.int64).reshape(-1)
+    if L.shape != (B,) or (L < 0).any() or (L > Nk).any():
+        raise ValueError(f"seqlens_k must be {B} lengths in [0, {Nk}]")
+    return L
+
+
+def _bias_view(bias, B: int, Hq: int, Nq: int, Nk: int):
+    """Callable (b, hq) -> the [Nq, Nk] bias slice, broadcasting a size-1 batch or head dim."""
+    if bias is None:
+        return None
+    bias = np.asarray(bias, dtype=np.float64)
+    Bb, Hb = bias.shape[0], bias.shape[1]
+    if bias.ndim != 4 or Bb not in (1, B) or Hb not in (1, Hq) or bias.shape[2:] != (Nq, Nk):
+        raise ValueError(f"bias must be [1 or {B}, 1 or {Hq}, {Nq}, {Nk}], got {bias.shape}")
+    return lambda b, hq: bias[b if Bb == B else 0, hq if Hb == Hq else 0]
+
+
+def _row_scores(qrows, kh, scale, bias_rows):
+    """Scaled scores of some query rows against the keys ``kh``, plus the bias rows if any."""
+    s = _scores(qrows, kh, scale)
+    return s if bias_rows is None else s + bias_rows
+
+
+def attention_fp64(q, k, v, scale: float, causal: bool, row_block: int = 1024, bias=None,
+                   seqlens_k=None) -> Tuple[np.ndarray, np.ndarray]:
+    """O [B,Hq,Nq,d] and LSE [B,Hq,Nq] of softmax(scale·q·kᵀ + bias + causal mask)·v, in fp64.
 
     ``scale`` is the float the GPU receives (0 selects 1/√d); it is widened to fp64 unchanged.
+    ``bias`` and ``seqlens_k`` are optional (see the module docstring for their readings).
     Rows are processed ``row_block`` at a time only to bound memory; rows are independent.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -110,22 +147,28 @@ def attention_fp64(q, k, v, scale: float, causal: bool, row_block: int = 1024
     v = np.asarray(v, dtype=np.float64)
     B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
     scale = _resolve_scale(scale, d)
+    L = _key_lengths(seqlens_k, B, Nk)
+    bview = _bias_view(bias, B, Hq, Nq, Nk)
     out = np.zeros((B, Hq, Nq, d), dtype=np.float64)
     lse = np.full((B, Hq, Nq), NEG_INF, dtype=np.float64)
     for b in range(B):
+        Lb = int(L[b])
+        if Lb == 0:
+            continue  # no key at all: O = 0, LSE = -inf
         for hq in range(Hq):
             hkv = _kv_head(hq, Hq, Hkv)
             for i0 in range(0, Nq, row_block):
                 rows = np.arange(i0, min(Nq, i0 + row_block))
-                s = _scores(q[b, hq, rows], k[b, hkv], scale)
-                vis = visible_mask(rows, Nq, Nk, causal)
+                brows = None if bview is None else bview(b, hq)[rows, :Lb]
+                s = _row_scores(q[b, hq, rows], k[b, hkv, :Lb], scale, brows)
+                vis = visible_mask(rows, Nq, Lb, causal)
                 p, m, l = _masked_softmax(s, vis)
-                out[b, hq, rows] = _weighted_values(p, v[b, hkv])
+                out[b, hq, rows] = _weighted_values(p, v[b, hkv, :Lb])
                 lse[b, hq, rows] = _row_lse(m, l)
     return out, lse
 
 
-def attention_rows_fp64(q, k, v, scale: float, causal: bool, rows
+def attention_rows_fp64(q, k, v, scale: float, causal: bool, rows, bias=None, seqlens_k=None
                         ) -> Tuple[np.ndarray, np.ndarray]:
     """Only the query rows ``rows`` (positions in 0..Nq-1, same for every batch and head) of
     ``attention_fp64``: O [B,Hq,len(rows),d], LSE [B,Hq,len(rows)].  The causal mask uses each
@@ -135,17 +178,23 @@ def attention_rows_fp64(q, k, v, scale: float, causal: bool, rows
     v = np.asarray(v, dtype=np.float64)
     B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
     scale = _resolve_scale(scale, d)
+    L = _key_lengths(seqlens_k, B, Nk)
+    bview = _bias_view(bias, B, Hq, Nq, Nk)
     rows = np.asarray(rows, dtype=np.int64)
     if rows.ndim != 1 or (len(rows) and (rows.min() < 0 or rows.max() >= Nq)):
         raise ValueError("rows must be positions in [0, Nq)")
     out = np.zeros((B, Hq, len(rows), d))
     lse = np.full((B, Hq, len(rows)), NEG_INF)
     for b in range(B):
+        Lb = int(L[b])
+        if Lb == 0:
+            continue
         for hq in range(Hq):
             hkv = _kv_head(hq, Hq, Hkv)
-            s = _scores(q[b, hq, rows], k[b, hkv], scale)
-            p, m, l = _masked_softmax(s, visible_mask(rows, Nq, Nk, causal))
-            out[b, hq] = _weighted_values(p, v[b, hkv])
+            brows = None if bview is None else bview(b, hq)[rows, :Lb]
+            s = _row_scores(q[b, hq, rows], k[b, hkv, :Lb], scale, brows)
+            p, m, l = _masked_softmax(s, visible_mask(rows, Nq, Lb, causal))
+            out[b, hq] = _weighted_values(p, v[b, hkv, :Lb])
             lse[b, hq] = _row_lse(m, l)
     return out, lse
 
@@ -174,33 +223,40 @@ def split_bounds(Nk: int, n_splits: int):
     return [(min(s * L, Nk), min((s + 1) * L, Nk)) for s in range(n_splits)]
 
 
-def splitkv_partials_fp64(q, k, v, scale: float, causal: bool, n_splits: int):
+def splitkv_partials_fp64(q, k, v, scale: float, causal: bool, n_splits: int, bias=None,
+                          seqlens_k=None):
     """Per-split partials of the decode model.
 
     Returns (O_s [B,Hq,Nq,S,d], m_s [B,Hq,Nq,S], l_s [B,Hq,Nq,S]): for split s and row i,
     m_s is the max scaled visible score in the chunk, l_s = Σ exp(score - m_s) over the chunk, and
     O_s = Σ exp(score - m_s)·v / l_s (locally normalised).  Empty or fully masked chunks give
-    m_s = -inf, l_s = 0, O_s = 0.
+    m_s = -inf, l_s = 0, O_s = 0.  Chunks are those of the capacity Nk, clipped to each batch
+    element's key length when ``seqlens_k`` is given.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
     scale = _resolve_scale(scale, d)
+    L = _key_lengths(seqlens_k, B, Nk)
+    bview = _bias_view(bias, B, Hq, Nq, Nk)
     bounds = split_bounds(Nk, n_splits)
     S = len(bounds)
     O_s = np.zeros((B, Hq, Nq, S, d))
     m_s = np.full((B, Hq, Nq, S), NEG_INF)
     l_s = np.zeros((B, Hq, Nq, S))
     rows = np.arange(Nq)
-    vis_all = visible_mask(rows, Nq, Nk, causal)
     for b in range(B):
+        Lb = int(L[b])
+        vis_all = visible_mask(rows, Nq, Lb, causal)
         for hq in range(Hq):
             hkv = _kv_head(hq, Hq, Hkv)
-            for si, (k0, k1) in enumerate(bounds):
+            for si, (c0, c1) in enumerate(bounds):
+                k0, k1 = min(c0, Lb), min(c1, Lb)
                 if k1 <= k0:
                     continue
-                s = _scores(q[b, hq], k[b, hkv, k0:k1], scale)
+                brows = None if bview is None else bview(b, hq)[:, k0:k1]
+                s = _row_scores(q[b, hq], k[b, hkv, k0:k1], scale, brows)
                 p, m, l = _masked_softmax(s, vis_all[:, k0:k1])
                 O_s[b, hq, :, si] = _weighted_values(p, v[b, hkv, k0:k1])
                 m_s[b, hq, :, si] = m

@@ -325,6 +325,150 @@ def pin_row_subset_equals_full_rows():
                1e-14, "row subset prefix mean")
 
 
+# ---- per-batch key lengths and attention bias -----------------------------------------------
+
+def _brute_general(q, k, v, scale, causal, lengths=None, bias=None):
+    """Scalar Python with per-batch key lengths L_b (keys j < L_b exist, causal visibility
+    j <= i + L_b - Nq) and an additive bias bias[b|0, h|0, i, j] on the scaled score."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
+    O = np.zeros((B, Hq, Nq, dv))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        Lb = Nk if lengths is None else int(lengths[b])
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            for i in range(Nq):
+                w = []
+                for j in range(Lb):
+                    if causal and j > i + (Lb - Nq):
+                        continue
+                    sc = scale * math.fsum(float(q[b, h, i, t]) * float(k[b, hk, j, t])
+                                           for t in range(d))
+                    if bias is not None:
+                        sc += float(bias[b if bias.shape[0] > 1 else 0,
+                                         h if bias.shape[1] > 1 else 0, i, j])
+                    w.append((math.exp(sc), j))
+                if not w:
+                    continue
+                z = math.fsum(e for e, _ in w)
+                lse[b, h, i] = math.log(z)
+                for t in range(dv):
+                    O[b, h, i, t] = math.fsum(e * float(v[b, hk, j, t]) for e, j in w) / z
+    return O, lse
+
+
+def pin_varlen_brute_force():
+    B, Hq, Hkv, Nq, Nk, d = 4, 2, 1, 3, 6, 4
+    q, k, v = _rand(600, B, Hq, Nq, d), _rand(601, B, Hkv, Nk, d), _rand(602, B, Hkv, Nk, d)
+    L = np.array([6, 2, 0, 4])
+    for causal in (False, True):
+        O, lse = A.attention_fp64(q, k, v, 0.5, causal, seqlens_k=L)
+        Ob, lseb = _brute_general(q, k, v, 0.5, causal, lengths=L)
+        _close(O, Ob, 1e-12, "varlen brute force O")
+        _close(lse, lseb, 1e-12, "varlen brute force lse")
+        rows = np.array([0, 2])
+        Or, lr = A.attention_rows_fp64(q, k, v, 0.5, causal, rows, seqlens_k=L)
+        _close(Or, Ob[:, :, rows], 1e-12, "varlen rows O")
+        _close(lr, lseb[:, :, rows], 1e-12, "varlen rows lse")
+
+
+def pin_varlen_ignores_keys_past_length():
+    """Keys at or past L_b do not exist: replacing them by anything changes nothing."""
+    B, Hq, Hkv, Nq, Nk, d = 3, 4, 2, 5, 9, 8
+    q, k, v = _rand(610, B, Hq, Nq, d), _rand(611, B, Hkv, Nk, d), _rand(612, B, Hkv, Nk, d)
+    L = np.array([9, 5, 7])
+    k2, v2 = k.copy(), v.copy()
+    for b in range(B):
+        k2[b, :, L[b]:] = 1e3 * _rand(613 + b, Hkv, Nk - L[b], d)
+        v2[b, :, L[b]:] = -7.0
+    for causal in (False, True):
+        O1, l1 = A.attention_fp64(q, k, v, 0.3, causal, seqlens_k=L)
+        O2, l2 = A.attention_fp64(q, k2, v2, 0.3, causal, seqlens_k=L)
+        _close(O1, O2, 0.0, "varlen past-length O")
+        _close(l1, l2, 0.0, "varlen past-length lse")
+
+
+def pin_varlen_closed_forms():
+    """L_b = 0: O = 0, LSE = -inf.  L_b = 1: every row sees key 0 only (non-causal, or causal
+    rows i >= Nq - 1), so O = v_0 and LSE = scale·q·k_0; the other causal rows see nothing."""
+    B, Hq, Hkv, Nq, Nk, d = 2, 2, 2, 4, 6, 8
+    q, k, v = _rand(620, B, Hq, Nq, d), _rand(621, B, Hkv, Nk, d), _rand(622, B, Hkv, Nk, d)
+    L = np.array([0, 1])
+    for causal in (False, True):
+        O, lse = A.attention_fp64(q, k, v, 0.7, causal, seqlens_k=L)
+        assert np.all(O[0] == 0) and np.all(np.isneginf(lse[0])), "L = 0 row not empty"
+        for h in range(Hq):
+            for i in range(Nq):
+                if causal and i < Nq - 1:
+                    assert np.all(O[1, h, i] == 0) and np.isneginf(lse[1, h, i])
+                    continue
+                _close(O[1, h, i], v[1, h, 0], 1e-15, "L = 1 output")
+                _close(lse[1, h, i], 0.7 * float(q[1, h, i] @ k[1, h, 0]), 1e-13, "L = 1 lse")
+
+
+def pin_varlen_split_combine():
+    B, Hq, Hkv, Nq, Nk, d = 3, 4, 2, 4, 37, 8
+    q, k, v = _rand(630, B, Hq, Nq, d), _rand(631, B, Hkv, Nk, d), _rand(632, B, Hkv, Nk, d)
+    L = np.array([37, 11, 0])
+    for causal in (False, True):
+        for S in (1, 3, 5, 37):
+            O_s, m_s, l_s = A.splitkv_partials_fp64(q, k, v, 0.4, causal, S, seqlens_k=L)
+            Oc, lc = A.combine_fp64(O_s, m_s, l_s)
+            Ob, lb = _brute_general(q, k, v, 0.4, causal, lengths=L)
+            _close(Oc, Ob, 1e-12, f"varlen split/combine O S={S}")
+            _close(lc, lb, 1e-12, f"varlen split/combine lse S={S}")
+
+
+def pin_bias_brute_force():
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 3, 5, 4
+    q, k, v = _rand(640, B, Hq, Nq, d), _rand(641, B, Hkv, Nk, d), _rand(642, B, Hkv, Nk, d)
+    L = np.array([5, 3])
+    for shape in ((1, 1), (B, 1), (1, Hq), (B, Hq)):
+        bias = _rand(643 + shape[0] + 3 * shape[1], shape[0], shape[1], Nq, Nk)
+        for causal in (False, True):
+            for lengths in (None, L):
+                O, lse = A.attention_fp64(q, k, v, 0.6, causal, bias=bias, seqlens_k=lengths)
+                Ob, lseb = _brute_general(q, k, v, 0.6, causal, lengths=lengths, bias=bias)
+                _close(O, Ob, 1e-12, f"bias brute force O {shape}")
+                _close(lse, lseb, 1e-12, f"bias brute force lse {shape}")
+                O_s, m_s, l_s = A.splitkv_partials_fp64(q, k, v, 0.6, causal, 2, bias=bias,
+                                                        seqlens_k=lengths)
+                Oc, lc = A.combine_fp64(O_s, m_s, l_s)
+                _close(Oc, Ob, 1e-12, f"bias split/combine O {shape}")
+                _close(lc, lseb, 1e-12, f"bias split/combine lse {shape}")
+
+
+def pin_bias_row_shift():
+    """Adding c_i to every bias entry of row i leaves O unchanged and adds c_i to LSE."""
+    B, Hq, Hkv, Nq, Nk, d = 2, 2, 1, 6, 10, 8
+    q, k, v = _rand(650, B, Hq, Nq, d), _rand(651, B, Hkv, Nk, d), _rand(652, B, Hkv, Nk, d)
+    bias = _rand(653, B, Hq, Nq, Nk)
+    c = 3.0 * _rand(654, B, Hq, Nq)
+    for causal in (False, True):
+        O1, l1 = A.attention_fp64(q, k, v, 0.25, causal, bias=bias)
+        O2, l2 = A.attention_fp64(q, k, v, 0.25, causal, bias=bias + c[..., None])
+        _close(O1, O2, 1e-12, "bias row shift O")
+        _close(l1 + c, l2, 1e-12, "bias row shift lse")
+
+
+def pin_bias_rank_one_is_extra_head_dim():
+    """A bias scale·u_i·w_j equals one more head dimension (q_i, u_i)·(k_j, w_j) at the same
+    scale, with no bias."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 2, 2, 5, 7, 6
+    q, k, v = _rand(660, B, Hq, Nq, d), _rand(661, B, Hkv, Nk, d), _rand(662, B, Hkv, Nk, d)
+    u, w = _rand(663, B, Hq, Nq), _rand(664, B, Hkv, Nk)
+    bias = 0.35 * u[..., :, None] * w[..., None, :]
+    qa = np.concatenate([q, u[..., None]], axis=-1)
+    ka = np.concatenate([k, w[..., None]], axis=-1)
+    va = v
+    for causal in (False, True):
+        O1, l1 = A.attention_fp64(q, k, v, 0.35, causal, bias=bias)
+        Ob, lb = _brute_general(qa, ka, va, 0.35, causal)
+        _close(O1, Ob, 1e-12, "rank-one bias O")
+        _close(l1, lb, 1e-12, "rank-one bias lse")
+
+
 ALL_PINS = [
     pin_probs_rows_sum_to_one,
     pin_constant_values,
@@ -343,4 +487,11 @@ ALL_PINS = [
     pin_tiled_recurrence_equals_definition,
     pin_decode_rows_equal_prefill_rows,
     pin_row_subset_equals_full_rows,
+    pin_varlen_brute_force,
+    pin_varlen_ignores_keys_past_length,
+    pin_varlen_closed_forms,
+    pin_varlen_split_combine,
+    pin_bias_brute_force,
+    pin_bias_row_shift,
+    pin_bias_rank_one_is_extra_head_dim,
 ]

@@ -47,9 +47,32 @@ def _combine_no_exp(O_s, m_s, l_s):
     return _ORIG["combine_fp64"](O_s, np.where(np.isfinite(m_s), 0.0, m_s), l_s)
 
 
-def _partials_unnormalised(q, k, v, scale, causal, n_splits):
-    O_s, m_s, l_s = _ORIG["splitkv_partials_fp64"](q, k, v, scale, causal, n_splits)
+def _partials_unnormalised(q, k, v, scale, causal, n_splits, **kw):
+    O_s, m_s, l_s = _ORIG["splitkv_partials_fp64"](q, k, v, scale, causal, n_splits, **kw)
     return O_s * l_s[..., None], m_s, l_s
+
+
+def _bias_scaled(qrows, kh, scale, bias_rows):
+    s = _ORIG["_scores"](qrows, kh, scale)
+    return s if bias_rows is None else s + scale * bias_rows
+
+
+def _key_lengths_capacity(seqlens_k, B, Nk):
+    return np.full(B, Nk, dtype=np.int64)
+
+
+def _key_lengths_minus_one(seqlens_k, B, Nk):
+    L = _ORIG["_key_lengths"](seqlens_k, B, Nk)
+    return L if seqlens_k is None else np.maximum(L - 1, 0)
+
+
+def _bias_transposed_heads(bias, B, Hq, Nq, Nk):
+    view = _ORIG["_bias_view"](bias, B, Hq, Nq, Nk)
+    if view is None:
+        return None
+    bias = np.asarray(bias, dtype=np.float64)
+    return lambda b, hq: bias[0 if bias.shape[0] == 1 else b, 0 if bias.shape[1] == 1 else
+                              (Hq - 1 - hq)]
 
 
 MUTANTS = {
@@ -82,6 +105,13 @@ MUTANTS = {
     "online_l_not_rescaled": ("_online_step", _online_no_rescale_l),
     "combine_without_exp": ("combine_fp64", _combine_no_exp),
     "partials_unnormalised": ("splitkv_partials_fp64", _partials_unnormalised),
+    "bias_dropped": ("_row_scores", lambda qr, kh, scale, br: _ORIG["_scores"](qr, kh, scale)),
+    "bias_scaled": ("_row_scores", _bias_scaled),
+    "bias_subtracted": ("_row_scores", lambda qr, kh, scale, br: _ORIG["_scores"](qr, kh, scale)
+                        if br is None else _ORIG["_scores"](qr, kh, scale) - br),
+    "bias_heads_reversed": ("_bias_view", _bias_transposed_heads),
+    "seqlens_ignored": ("_key_lengths", _key_lengths_capacity),
+    "seqlens_off_by_one": ("_key_lengths", _key_lengths_minus_one),
 }
 
 _ORIG = {name: getattr(A, name) for name, _ in MUTANTS.values()}
