@@ -32,7 +32,9 @@ Readings where the pages are silent (each applied identically everywhere):
 * Attention bias (the same page, section "1. 커널 퓨전": the fused decode kernel applies the
   attention bias and the causal mask after QKᵀ, with bias dimensions 0 and 1 broadcast): a
   tensor [Bb, Hb, Nq, Nk] with Bb in {1, B} and Hb in {1, Hq} is added to the scaled scores
-  before masking: s = scale·q·kᵀ + bias.
+  before masking: s = scale·q·kᵀ + bias.  A -inf entry masks its key exactly as the causal fill
+  does (section 1 of the PyTorch page writes masked positions as -inf), so a row whose every
+  key is masked this way is a row with no visible key.
 
 All arithmetic is numpy float64; the matrix product (``@``) is the only library primitive.
 """
@@ -75,12 +77,14 @@ def _masked_softmax(s: np.ndarray, vis: np.ndarray):
     """Steps 3-4: fill invisible scores with -inf, then row softmax.
 
     Returns (P, m, l) with m the row max over visible scores and l = sum exp(s - m); rows with no
-    visible key get P = 0, m = -inf, l = 0.
+    visible key get P = 0, m = -inf, l = 0.  A score that is already -inf (a -inf bias entry) is
+    a masked key like any other, so a row whose every score is -inf has no visible key.
     """
     s = np.where(vis, s, NEG_INF)
-    any_vis = vis.any(axis=1)
+    live = vis & ~np.isneginf(s)
+    any_vis = live.any(axis=1)
     m = np.where(any_vis, s.max(axis=1, initial=NEG_INF), NEG_INF)
-    shifted = np.where(vis, s - np.where(any_vis, m, 0.0)[:, None], NEG_INF)
+    shifted = np.where(live, s - np.where(any_vis, m, 0.0)[:, None], NEG_INF)
     e = np.exp(shifted)  # exp(-inf) = 0 for invisible entries
     l = e.sum(axis=1)
     p = np.divide(e, l[:, None], out=np.zeros_like(e), where=(l[:, None] > 0))

@@ -469,6 +469,30 @@ def pin_bias_rank_one_is_extra_head_dim():
         _close(l1, lb, 1e-12, "rank-one bias lse")
 
 
+def pin_bias_neg_inf_is_mask():
+    """A bias that is -inf exactly where the causal mask hides a key and 0 elsewhere gives the
+    causal result with no bias; a row biased to -inf everywhere has no visible key."""
+    B, Hq, Hkv, Nq, Nk, d = 2, 3, 1, 5, 9, 4
+    q, k, v = _rand(670, B, Hq, Nq, d), _rand(671, B, Hkv, Nk, d), _rand(672, B, Hkv, Nk, d)
+    rows, cols = np.arange(Nq)[:, None], np.arange(Nk)[None, :]
+    bias = np.where(cols <= rows + (Nk - Nq), 0.0, -np.inf)[None, None]
+    Oc, lc = A.attention_fp64(q, k, v, 0.5, True)
+    Ob, lb = A.attention_fp64(q, k, v, 0.5, False, bias=bias)
+    _close(Ob, Oc, 1e-12, "-inf bias as causal mask O")
+    _close(lb, lc, 1e-12, "-inf bias as causal mask lse")
+    O_s, m_s, l_s = A.splitkv_partials_fp64(q, k, v, 0.5, False, 3, bias=bias)
+    Os, ls = A.combine_fp64(O_s, m_s, l_s)
+    _close(Os, Oc, 1e-12, "-inf bias as causal mask, split O")
+    _close(ls, lc, 1e-12, "-inf bias as causal mask, split lse")
+    full = np.zeros((1, Hq, Nq, Nk))
+    full[0, 1, 2, :] = -np.inf
+    O, lse = A.attention_fp64(q, k, v, 0.5, False, bias=full)
+    assert np.all(O[:, 1, 2] == 0.0) and np.all(lse[:, 1, 2] == -np.inf), "all -inf row"
+    assert np.isfinite(O).sum() == O.size and np.isfinite(lse).sum() == lse.size - B
+    O_s, m_s, l_s = A.splitkv_partials_fp64(q, k, v, 0.5, False, 2, bias=full)
+    assert np.all(l_s[:, 1, 2] == 0.0) and np.all(m_s[:, 1, 2] == -np.inf), "all -inf split"
+
+
 ALL_PINS = [
     pin_probs_rows_sum_to_one,
     pin_constant_values,
@@ -494,4 +518,5 @@ ALL_PINS = [
     pin_bias_brute_force,
     pin_bias_row_shift,
     pin_bias_rank_one_is_extra_head_dim,
+    pin_bias_neg_inf_is_mask,
 ]
