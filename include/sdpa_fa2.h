@@ -64,7 +64,8 @@ enum {
   ATTN_ERR_SCALE = -6,     /* scale is negative, NaN or infinite */
   ATTN_ERR_SPLITS = -7,    /* n_splits < 1 or n_splits > max(Nk, 1) */
   ATTN_ERR_WORKSPACE = -8, /* workspace NULL or smaller than attn_decode_workspace_bytes() */
-  ATTN_ERR_LAUNCH = -9     /* the HIP runtime rejected a kernel launch */
+  ATTN_ERR_LAUNCH = -9,    /* the HIP runtime rejected a kernel launch */
+  ATTN_ERR_BIAS = -10      /* bias_b not 1 or B, bias_h not 1 or Hq, or Nk % 4 != 0 with a bias */
 };
 
 /*
@@ -122,6 +123,76 @@ SDPA_FA2_API int attn_decode_splitkv(const void* q, const void* k, const void* v
                         void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int Nq, int Nk, int d,
                         float scale, int causal, int n_splits, void* stream);
+
+/*
+ * Extras of the *_ex entry points and of attn_forward (all optional: NULL means "none").
+ *
+ * seqlens_k  DEVICE pointer to int32 [B], 4-byte aligned, or NULL.  seqlens_k[b] is the number of
+ *            valid keys of batch element b: only K/V rows 0 .. seqlens_k[b]-1 exist for it, and
+ *            the causal mask is aligned to the end of those keys (key j visible to query i iff
+ *            j <= i + seqlens_k[b] - Nq).  Nk is then the capacity (the seq dimension of k and
+ *            v).  Values are read on the device and clamped to [0, Nk]; a batch element with no
+ *            key gets out = 0 and lse = -inf.  These are the per-batch KV lengths that the
+ *            onnxruntime WebGPU page's decode path reads on the GPU ("[onnxruntime] WebGPU
+ *            FlashAttention 최적화: 커널 퓨전과 가변 시퀀스 길이 지원으로 성능 극대화", the varlen part
+ *            of its title and its seqlens_k inputs).  Split-KV chunks stay those of the capacity
+ *            Nk, clipped to each element's length.
+ * bias       DEVICE pointer to bf16 [bias_b, bias_h, Nq, Nk], contiguous, 16-byte aligned, or
+ *            NULL; bias_b is 1 or B and bias_h is 1 or Hq (a size-1 dimension is broadcast), and
+ *            Nk must be a multiple of 4.  The bias is added to the scaled scores before the mask
+ *            (s = scale * q.k + bias), the attention bias of the same page's fused decode program
+ *            (section 1); a -inf entry masks its key.  With seqlens_k, bias columns at or past
+ *            seqlens_k[b] are never read.  bias_b / bias_h are ignored when bias is NULL.
+ *
+ * Errors added by the extras: ATTN_ERR_BIAS (dims or Nk % 4) and ATTN_ERR_ALIGN (alignment).
+ */
+
+/*
+ * attn_fwd_ex -- attn_fwd with per-batch key lengths and an additive bias (see above).  With
+ * seqlens_k == NULL and bias == NULL it is exactly attn_fwd.  bfloat16 tensors only.
+ */
+SDPA_FA2_API int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                const int* seqlens_k, const void* bias, int bias_b, int bias_h,
+                int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                float scale, int causal, void* stream);
+
+/*
+ * attn_decode_splitkv_ex -- attn_decode_splitkv with per-batch key lengths and an additive bias
+ * (see above).  Same workspace contract as attn_decode_splitkv.
+ */
+SDPA_FA2_API int attn_decode_splitkv_ex(const void* q, const void* k, const void* v, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           const int* seqlens_k, const void* bias, int bias_b, int bias_h,
+                           int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                           float scale, int causal, int n_splits, void* stream);
+
+/*
+ * attn_decode_num_splits -- the split count attn_forward uses for split-KV: enough workgroups
+ * (B * Hkv * ceil(Hq/Hkv * Nq / 16) per split) for about 1024 in all, but no split shorter than
+ * 256 keys, and at most 256 splits.  Returns 1 for degenerate or invalid arguments.
+ */
+SDPA_FA2_API int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk);
+
+/*
+ * attn_forward_workspace_bytes -- workspace attn_forward needs for these sizes: 0 when it takes
+ * the prefill kernel (Nq >= 32), else attn_decode_workspace_bytes with attn_decode_num_splits.
+ */
+SDPA_FA2_API size_t attn_forward_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/*
+ * attn_forward -- one entry for any query length, with the routing rule of the onnxruntime
+ * WebGPU page (section "3. 경로 라우팅 최적화": split-reduce below 32 query rows, the prefill
+ * program otherwise):
+ *   Nq <  32 (and Nk >= 1): attn_decode_splitkv_ex with attn_decode_num_splits splits; the
+ *            workspace must hold attn_forward_workspace_bytes bytes.
+ *   Nq >= 32 (or Nk == 0):  attn_fwd_ex; workspace is not used and may be NULL.
+ * Arguments and errors as for those two entry points.
+ */
+SDPA_FA2_API int attn_forward(const void* q, const void* k, const void* v, void* out, float* lse,
+                 void* workspace, size_t workspace_bytes,
+                 const int* seqlens_k, const void* bias, int bias_b, int bias_h,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, void* stream);
 
 /* attn_status_string -- a static, NUL-terminated description of a status code. */
 SDPA_FA2_API const char* attn_status_string(int status);

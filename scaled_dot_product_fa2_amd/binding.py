@@ -25,6 +25,14 @@ _SIGNATURES = {
     "attn_decode_workspace_bytes": (_c_size, [_c_int] * 5),
     "attn_decode_splitkv": (_c_int, [_vp] * 6 + [_c_size] + [_c_int] * 6 +
                             [_c_float, _c_int, _c_int, _vp]),
+    "attn_fwd_ex": (_c_int, [_vp] * 5 + [_vp, _vp, _c_int, _c_int] + [_c_int] * 6 +
+                    [_c_float, _c_int, _vp]),
+    "attn_decode_splitkv_ex": (_c_int, [_vp] * 6 + [_c_size] + [_vp, _vp, _c_int, _c_int] +
+                               [_c_int] * 6 + [_c_float, _c_int, _c_int, _vp]),
+    "attn_decode_num_splits": (_c_int, [_c_int] * 5),
+    "attn_forward_workspace_bytes": (_c_size, [_c_int] * 6),
+    "attn_forward": (_c_int, [_vp] * 6 + [_c_size] + [_vp, _vp, _c_int, _c_int] + [_c_int] * 6 +
+                     [_c_float, _c_int, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_c_int]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -113,6 +121,28 @@ def _validate(q, k, v, dtype):
     return B, Hq, k.shape[1], Nq, k.shape[2], d
 
 
+def _extras(q, B, Hq, Nq, Nk, seqlens_k, bias):
+    """Marshal the optional per-batch key lengths (int32 [B]) and bias (bf16 [1|B, 1|Hq, Nq, Nk])
+    into (seqlens_ptr, bias_ptr, bias_b, bias_h); shape rules beyond these are the library's."""
+    import torch
+
+    sp = None
+    if seqlens_k is not None:
+        if (not isinstance(seqlens_k, torch.Tensor) or seqlens_k.dtype != torch.int32 or
+                seqlens_k.device != q.device or tuple(seqlens_k.shape) != (B,) or
+                not seqlens_k.is_contiguous()):
+            raise ValueError(f"seqlens_k must be a contiguous int32 [{B}] tensor on {q.device}")
+        sp = seqlens_k.data_ptr()
+    if bias is None:
+        return sp, None, 1, 1
+    if (not isinstance(bias, torch.Tensor) or bias.dtype != torch.bfloat16 or
+            bias.device != q.device or bias.dim() != 4 or not bias.is_contiguous() or
+            tuple(bias.shape[2:]) != (Nq, Nk)):
+        raise ValueError(f"bias must be a contiguous bf16 [1|B, 1|Hq, {Nq}, {Nk}] tensor on "
+                         f"{q.device}")
+    return sp, _ptr(bias), int(bias.shape[0]), int(bias.shape[1])
+
+
 def attn_fwd(q, k, v, causal: bool = True, scale: float = 0.0, out=None, lse=None,
              want_lse: bool = True) -> Tuple[object, object]:
     """Fused attention forward on bf16 [B,H,N,d] tensors; returns (out bf16, lse fp32 or None)."""
@@ -126,6 +156,24 @@ def attn_fwd(q, k, v, causal: bool = True, scale: float = 0.0, out=None, lse=Non
     rc = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                          float(scale), int(bool(causal)), _stream(q.device))
     _check_rc(rc, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_ex(q, k, v, causal: bool = True, scale: float = 0.0, seqlens_k=None, bias=None,
+                out=None, lse=None, want_lse: bool = True):
+    """``attn_fwd`` with optional per-batch key lengths (int32 [B] on the device) and an additive
+    bf16 bias [1|B, 1|Hq, Nq, Nk]; returns (out, lse)."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    sp, bp, bb, bh = _extras(q, B, Hq, Nq, Nk, seqlens_k, bias)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    rc = load().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), sp, bp, bb, bh, B, Hq,
+                            Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(q.device))
+    _check_rc(rc, "attn_fwd_ex")
     return out, lse
 
 
@@ -172,6 +220,62 @@ def attn_decode_splitkv(q, k, v, n_splits: int, causal: bool = True, scale: floa
                                     B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
                                     int(n_splits), _stream(q.device))
     _check_rc(rc, "attn_decode_splitkv")
+    return out, lse, workspace
+
+
+def attn_decode_splitkv_ex(q, k, v, n_splits: int, causal: bool = True, scale: float = 0.0,
+                           seqlens_k=None, bias=None, out=None, lse=None, workspace=None,
+                           want_lse: bool = True):
+    """``attn_decode_splitkv`` with optional per-batch key lengths and bias; returns
+    (out, lse, workspace)."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    sp, bp, bb, bh = _extras(q, B, Hq, Nq, Nk, seqlens_k, bias)
+    need = attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits) if n_splits >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    rc = load().attn_decode_splitkv_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                       _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), sp, bp, bb,
+                                       bh, B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                       int(bool(causal)), int(n_splits), _stream(q.device))
+    _check_rc(rc, "attn_decode_splitkv_ex")
+    return out, lse, workspace
+
+
+def attn_decode_num_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int) -> int:
+    return int(load().attn_decode_num_splits(B, Hq, Hkv, Nq, Nk))
+
+
+def attn_forward_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load().attn_forward_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
+
+
+def attn_forward(q, k, v, causal: bool = True, scale: float = 0.0, seqlens_k=None, bias=None,
+                 out=None, lse=None, workspace=None, want_lse: bool = True):
+    """One call for any query length: split-KV below 32 query rows, the prefill kernel otherwise
+    (the library decides); returns (out, lse, workspace)."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    sp, bp, bb, bh = _extras(q, B, Hq, Nq, Nk, seqlens_k, bias)
+    need = attn_forward_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
+                             ws_bytes, sp, bp, bb, bh, B, Hq, Hkv, Nq, Nk, d, float(scale),
+                             int(bool(causal)), _stream(q.device))
+    _check_rc(rc, "attn_forward")
     return out, lse, workspace
 
 

@@ -53,6 +53,53 @@ float resolve_scale(float scale, int d) { return scale == 0.f ? 1.0f / sqrtf((fl
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
+// Checks of the optional extras: per-batch key lengths and the additive bias.
+int check_extras(const int* seqlens_k, const void* bias, int bias_b, int bias_h, int B, int Hq,
+                 int Nk) {
+  if (seqlens_k != nullptr && !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGN;
+  if (bias == nullptr) return ATTN_OK;
+  if (!(bias_b == 1 || bias_b == B) || !(bias_h == 1 || bias_h == Hq)) return ATTN_ERR_BIAS;
+  if (Nk % 4 != 0) return ATTN_ERR_BIAS;
+  if (!aligned(bias, 16)) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+// Prefill: launch-size check, then the kernel
+int run_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+            const int* seqlens_k, const void* bias, int bias_b, int bias_h, int B, int Hq,
+            int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  const long long blocks = (long long)B * Hq * ((Nq + 127) / 128);
+  if (blocks > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
+  return launch_status(fa::launch_fwd_bf16(q, k, v, out, lse, seqlens_k, bias, bias_b, bias_h, s,
+                                           resolve_scale(scale, d), causal != 0,
+                                           (hipStream_t)stream));
+}
+
+// Split-KV decode after the common checks: split count, workspace, launch sizes
+int run_decode(const void* q, const void* k, const void* v, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, const int* seqlens_k, const void* bias,
+               int bias_b, int bias_h, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               float scale, int causal, int n_splits, bool empty, void* stream) {
+  if (n_splits < 1 || n_splits > (Nk > 1 ? Nk : 1)) return ATTN_ERR_SPLITS;
+  if (empty) return ATTN_OK;
+  const size_t need = attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits);
+  if (need == 0 || workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+  const long long R = (long long)(Hq / Hkv) * Nq;
+  const long long blocks = (long long)B * Hkv * ((R + 15) / 16) * n_splits;
+  const long long rows = (long long)B * Hq * Nq;
+  if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  float* ws_o = (float*)workspace;
+  float* ws_ml = ws_o + (size_t)rows * n_splits * d;
+  const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
+  return launch_status(fa::launch_decode_splitkv(q, k, v, out, lse, ws_o, ws_ml, seqlens_k, bias,
+                                                 bias_b, bias_h, s, resolve_scale(scale, d),
+                                                 causal != 0, n_splits, (hipStream_t)stream));
+}
+
+constexpr int kRouteDecodeBelow = 32;  // query rows below which attn_forward takes split-KV
+
 }  // namespace
 
 extern "C" {
@@ -62,11 +109,20 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   bool empty;
   int rc = check_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, &empty);
   if (rc != ATTN_OK || empty) return rc;
-  const long long blocks = (long long)B * Hq * ((Nq + 127) / 128);
-  if (blocks > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-  const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
-  return launch_status(fa::launch_fwd_bf16(q, k, v, out, lse, s, resolve_scale(scale, d),
-                                           causal != 0, (hipStream_t)stream));
+  return run_fwd(q, k, v, out, lse, nullptr, nullptr, 1, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                 stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                const int* seqlens_k, const void* bias, int bias_b, int bias_h, int B, int Hq,
+                int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  bool empty;
+  int rc = check_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, &empty);
+  if (rc != ATTN_OK) return rc;
+  rc = check_extras(seqlens_k, bias, bias_b, bias_h, B, Hq, Nk);
+  if (rc != ATTN_OK || empty) return rc;
+  return run_fwd(q, k, v, out, lse, seqlens_k, bias, bias_b, bias_h, B, Hq, Hkv, Nq, Nk, d, scale,
+                 causal, stream);
 }
 
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* out, float* lse, int B,
@@ -97,21 +153,52 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, void* out, 
   bool empty;
   int rc = check_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, &empty);
   if (rc != ATTN_OK) return rc;
-  if (n_splits < 1 || n_splits > (Nk > 1 ? Nk : 1)) return ATTN_ERR_SPLITS;
-  if (empty) return ATTN_OK;
-  const size_t need = attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits);
-  if (need == 0 || workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
-  const long long R = (long long)(Hq / Hkv) * Nq;
-  const long long blocks = (long long)B * Hkv * ((R + 15) / 16) * n_splits;
-  const long long rows = (long long)B * Hq * Nq;
-  if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return ATTN_ERR_SHAPE;
-  float* ws_o = (float*)workspace;
-  float* ws_ml = ws_o + (size_t)rows * n_splits * d;
-  const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
-  return launch_status(fa::launch_decode_splitkv(q, k, v, out, lse, ws_o, ws_ml, s,
-                                                 resolve_scale(scale, d), causal != 0, n_splits,
-                                                 (hipStream_t)stream));
+  return run_decode(q, k, v, out, lse, workspace, workspace_bytes, nullptr, nullptr, 1, 1, B, Hq,
+                    Hkv, Nq, Nk, d, scale, causal, n_splits, empty, stream);
+}
+
+int attn_decode_splitkv_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, const int* seqlens_k,
+                           const void* bias, int bias_b, int bias_h, int B, int Hq, int Hkv,
+                           int Nq, int Nk, int d, float scale, int causal, int n_splits,
+                           void* stream) {
+  bool empty;
+  int rc = check_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, &empty);
+  if (rc != ATTN_OK) return rc;
+  rc = check_extras(seqlens_k, bias, bias_b, bias_h, B, Hq, Nk);
+  if (rc != ATTN_OK) return rc;
+  return run_decode(q, k, v, out, lse, workspace, workspace_bytes, seqlens_k, bias, bias_b,
+                    bias_h, B, Hq, Hkv, Nq, Nk, d, scale, causal, n_splits, empty, stream);
+}
+
+int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0) return 1;
+  // enough workgroups to give every compute unit a few (4 x 256), but at least 256 keys (two
+  // 32-key blocks per wave) per split
+  const long long per_split = (long long)B * Hkv * (((long long)(Hq / Hkv) * Nq + 15) / 16);
+  const long long want = (1024 + per_split - 1) / per_split;
+  const long long most = ((long long)Nk + 255) / 256;
+  long long s = want < most ? want : most;
+  if (s < 1) s = 1;
+  if (s > 256) s = 256;
+  return (int)s;
+}
+
+size_t attn_forward_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (Nq >= kRouteDecodeBelow) return 0;
+  return attn_decode_workspace_bytes(B, Hq, Nq, d, attn_decode_num_splits(B, Hq, Hkv, Nq, Nk));
+}
+
+int attn_forward(const void* q, const void* k, const void* v, void* out, float* lse,
+                 void* workspace, size_t workspace_bytes, const int* seqlens_k, const void* bias,
+                 int bias_b, int bias_h, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, void* stream) {
+  if (Nq >= kRouteDecodeBelow || Nk < 1)
+    return attn_fwd_ex(q, k, v, out, lse, seqlens_k, bias, bias_b, bias_h, B, Hq, Hkv, Nq, Nk, d,
+                       scale, causal, stream);
+  return attn_decode_splitkv_ex(q, k, v, out, lse, workspace, workspace_bytes, seqlens_k, bias,
+                                bias_b, bias_h, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                                attn_decode_num_splits(B, Hq, Hkv, Nq, Nk), stream);
 }
 
 const char* attn_status_string(int status) {
@@ -126,6 +213,8 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_SPLITS: return "n_splits must be in [1, max(Nk, 1)]";
     case ATTN_ERR_WORKSPACE: return "decode workspace is NULL or too small";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+    case ATTN_ERR_BIAS:
+      return "bias dims must be 1 or B (batch) and 1 or Hq (heads), and Nk a multiple of 4";
     default: return "unknown status";
   }
 }

@@ -74,11 +74,12 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x + __shfl_xor(x, 16);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, float* __restrict__ wsO, float* __restrict__ wsML, int Hq,
-    int Hkv, int Nq, int Nk, int S, int L, int nrg, float scale, float scale_log2) {
+    const uint16_t* __restrict__ V, float* __restrict__ wsO, float* __restrict__ wsML,
+    const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
+    int Hq, int Hkv, int Nq, int Nk_cap, int S, int L, int nrg, float scale, float scale_log2) {
   using C = DecCfg<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
 
@@ -91,6 +92,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   n /= nrg;
   const int hkv = n % Hkv, b = n / Hkv;
   const int G = Hq / Hkv, R = G * Nq;
+  // keys of this batch element: all Nk_cap rows of K/V, or the first seqlens[b] (clamped); the
+  // split chunks are those of the capacity, clipped to it
+  const int Nk = seqlens ? min(max(seqlens[b], 0), Nk_cap) : Nk_cap;
   const int off = Nk - Nq;
 
   // this lane's query column: row r of the KV head's group = (query head offset g, position qi)
@@ -105,10 +109,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const int lim = CAUSAL ? min(ks1 - 1, qi + off) : ks1 - 1;  // last visible key of this row
 
   // buffer resources covering exactly this split's keys: rows past the split read as zero
-  const size_t split_off = (((size_t)b * Hkv + hkv) * Nk + ks0) * D;
+  const size_t split_off = (((size_t)b * Hkv + hkv) * Nk_cap + ks0) * D;
   const uint32_t split_bytes = (uint32_t)(ks1 - ks0) * D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + split_off, split_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + split_off, split_bytes);
+  // additive bias (bf16 [bias_b, bias_h, Nq, Nk_cap], broadcast over batch / heads when 1): a
+  // lane needs keys k0 + 16hh + 4grp + 0..3 of its own row, two 8-byte loads per block, issued
+  // with the block's K/V.  Groups of four never straddle a row (Nk_cap % 4 == 0); groups at or
+  // past the split end are not loaded (those keys are masked).
+  const uint16_t* brow =
+      BIAS ? bias + (((size_t)(bias_b == 1 ? 0 : b) * bias_h + (bias_h == 1 ? 0 : hq)) * Nq + qi) *
+                        Nk_cap
+           : nullptr;
+  const float inv_scale = 1.f / scale;
   uint16_t* kls = (uint16_t*)smem + wave * C::WTILE;
   uint16_t* vls = kls + C::KB * D;
 
@@ -116,12 +129,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   // -> this wave's LDS slice -> MFMA operands.  Chunk i of a lane is byte
   // (32 kb + lane / CPR + i * 64 / CPR) * 2D + (lane % CPR) * 16 of the split.
   const uint32_t lane_off = (uint32_t)(lane / C::CPR) * (D * 2) + (uint32_t)(lane % C::CPR) * 16;
-  auto gload = [&](u32x4 (&kst)[C::NCH], u32x4 (&vst)[C::NCH], int kb) {
+  auto gload = [&](u32x4 (&kst)[C::NCH], u32x4 (&vst)[C::NCH], u32x2 (&bst)[2], int kb) {
     const uint32_t voff = lane_off + (uint32_t)(C::KB * kb) * (D * 2);
 #pragma unroll
     for (int i = 0; i < C::NCH; ++i) {
       kst[i] = load_16_stream(krs, voff, i * 1024u);
       vst[i] = load_16_stream(vrs, voff, i * 1024u);
+    }
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = ks0 + C::KB * kb + 16 * hh + 4 * grp;
+        bst[hh] = (row_ok && key < ks1) ? *(const u32x2*)(brow + key) : u32x2{0u, 0u};
+      }
     }
   };
   auto swrite = [&](const u32x4 (&kst)[C::NCH], const u32x4 (&vst)[C::NCH]) {
@@ -135,9 +155,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   };
 
   u32x4 kA[C::NCH], vA[C::NCH], kB[C::NCH], vB[C::NCH];
+  u32x2 bA[2], bB[2];
   const int kb0 = wave;
-  if (kb0 < nkb) gload(kA, vA, kb0);
-  if (kb0 + C::NW < nkb) gload(kB, vB, kb0 + C::NW);
+  if (kb0 < nkb) gload(kA, vA, bA, kb0);
+  if (kb0 + C::NW < nkb) gload(kB, vB, bB, kb0 + C::NW);
 
   // Qᵀ as the B operand of Sᵀ = K·Qᵀ (16x16x32): lane holds query column l16, head-dim slots
   // 32c + 8grp .. +7.
@@ -158,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const int tr_j = l16 >> 2, tr_t = l16 & 3;
 
   // one staged block: scores, masked online softmax, Oᵀ += Vᵀ·Pᵀ
-  auto compute = [&](int kb) {
+  auto compute = [&](int kb, const u32x2 (&bst)[2]) {
     const int k0 = ks0 + C::KB * kb;
     // Sᵀ (32 keys x 16 queries) in two 16-key halves: sc[h][i] is key k0 + 16h + 4grp + i
     f32x4 sc[2];
@@ -171,6 +192,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
         const u32x4 a = *(const u32x4*)(kls + row * D + 8 * dk_chunk<D>(row, 4 * c + grp));
         sc[hh] = mfma16x16x32(a, qf[c], sc[hh]);
       }
+    }
+    if constexpr (BIAS) {  // in score units, before the mask
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = bst[hh][i >> 1];
+          sc[hh][i] += __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16)) * inv_scale;
+        }
     }
     if (k0 + C::KB - 1 > lim) {
 #pragma unroll
@@ -219,14 +249,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   for (int kb = kb0; kb < nkb; kb += 2 * C::NW) {
     swrite(kA, vA);
     wave_lds_sync();
-    if (kb + 2 * C::NW < nkb) gload(kA, vA, kb + 2 * C::NW);  // keeps two blocks in flight
-    compute(kb);
+    const u32x2 bc[2] = {bA[0], bA[1]};
+    if (kb + 2 * C::NW < nkb) gload(kA, vA, bA, kb + 2 * C::NW);  // keeps two blocks in flight
+    compute(kb, bc);
     wave_lds_sync();  // this block's LDS reads precede the next block's writes
     if (kb + C::NW < nkb) {
       swrite(kB, vB);
       wave_lds_sync();
-      if (kb + 3 * C::NW < nkb) gload(kB, vB, kb + 3 * C::NW);
-      compute(kb + C::NW);
+      const u32x2 bd[2] = {bB[0], bB[1]};
+      if (kb + 3 * C::NW < nkb) gload(kB, vB, bB, kb + 3 * C::NW);
+      compute(kb + C::NW, bd);
       wave_lds_sync();
     }
   }
@@ -361,10 +393,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   if (LSE != nullptr && lane == 0) LSE[row] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 hipError_t launch(const void* q, const void* k, const void* v, void* out, float* lse,
-                  float* ws_o, float* ws_ml, const AttnShape& sh, float scale, int S,
-                  hipStream_t stream) {
+                  float* ws_o, float* ws_ml, const int* seqlens, const void* bias, int bias_b,
+                  int bias_h, const AttnShape& sh, float scale, int S, hipStream_t stream) {
   using C = DecCfg<D>;
   const int L = (sh.Nk + S - 1) / S;
   const int R = (sh.Hq / sh.Hkv) * sh.Nq;
@@ -372,9 +404,10 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, float*
   const long long blocks = (long long)sh.B * sh.Hkv * nrg * S;
   const long long rows = (long long)sh.B * sh.Hq * sh.Nq;
   if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(C::NT), 0,
-                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws_o,
-                     ws_ml, sh.Hq, sh.Hkv, sh.Nq, sh.Nk, S, L, nrg, scale, scale * kLog2e);
+  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, BIAS>), dim3((unsigned)blocks), dim3(C::NT),
+                     0, stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws_o,
+                     ws_ml, seqlens, (const uint16_t*)bias, bias_b, bias_h, sh.Hq, sh.Hkv, sh.Nq,
+                     sh.Nk, S, L, nrg, scale, scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)rows), dim3(64), 0,
@@ -383,17 +416,31 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, float*
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_b(const void* q, const void* k, const void* v, void* out, float* lse,
+                    float* ws_o, float* ws_ml, const int* seqlens, const void* bias, int bias_b,
+                    int bias_h, const AttnShape& s, float scale, int S, hipStream_t stream) {
+  return bias ? launch<D, CAUSAL, true>(q, k, v, out, lse, ws_o, ws_ml, seqlens, bias, bias_b,
+                                        bias_h, s, scale, S, stream)
+              : launch<D, CAUSAL, false>(q, k, v, out, lse, ws_o, ws_ml, seqlens, nullptr, 1, 1,
+                                         s, scale, S, stream);
+}
+
 }  // namespace
 
 hipError_t launch_decode_splitkv(const void* q, const void* k, const void* v, void* out,
-                                 float* lse, float* ws_o, float* ws_ml, const AttnShape& s,
+                                 float* lse, float* ws_o, float* ws_ml, const int* seqlens,
+                                 const void* bias, int bias_b, int bias_h, const AttnShape& s,
                                  float scale, bool causal, int n_splits, hipStream_t stream) {
   if (s.d == 128)
-    return causal ? launch<128, true>(q, k, v, out, lse, ws_o, ws_ml, s, scale, n_splits, stream)
-                  : launch<128, false>(q, k, v, out, lse, ws_o, ws_ml, s, scale, n_splits,
-                                       stream);
-  return causal ? launch<64, true>(q, k, v, out, lse, ws_o, ws_ml, s, scale, n_splits, stream)
-                : launch<64, false>(q, k, v, out, lse, ws_o, ws_ml, s, scale, n_splits, stream);
+    return causal ? launch_b<128, true>(q, k, v, out, lse, ws_o, ws_ml, seqlens, bias, bias_b,
+                                        bias_h, s, scale, n_splits, stream)
+                  : launch_b<128, false>(q, k, v, out, lse, ws_o, ws_ml, seqlens, bias, bias_b,
+                                         bias_h, s, scale, n_splits, stream);
+  return causal ? launch_b<64, true>(q, k, v, out, lse, ws_o, ws_ml, seqlens, bias, bias_b, bias_h,
+                                     s, scale, n_splits, stream)
+                : launch_b<64, false>(q, k, v, out, lse, ws_o, ws_ml, seqlens, bias, bias_b,
+                                      bias_h, s, scale, n_splits, stream);
 }
 
 }  // namespace fa

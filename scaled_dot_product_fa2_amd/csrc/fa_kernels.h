@@ -13,8 +13,10 @@ struct AttnShape {
   int B, Hq, Hkv, Nq, Nk, d;
 };
 
-// Prefill forward, bf16 tensors (fwd_bf16.hip).
+// Prefill forward, bf16 tensors (fwd_bf16.hip).  seqlens: NULL or device int32 [B] key counts;
+// bias: NULL or bf16 [bias_b, bias_h, Nq, Nk] (Nk % 4 == 0, 16-byte aligned base).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int* seqlens, const void* bias, int bias_b, int bias_h,
                            const AttnShape& s, float scale, bool causal, hipStream_t stream);
 
 // Prefill forward, fp32 tensors (fwd_f32.hip).
@@ -23,9 +25,11 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           hipStream_t stream);
 
 // Split-KV decode: split kernel then combine kernel on `stream` (decode.hip).
-// ws_o: fp32 [B, Hq, Nq, n_splits, d]; ws_ml: fp32 [B, Hq, Nq, n_splits, 2].
+// ws_o: fp32 [B, Hq, Nq, n_splits, d]; ws_ml: fp32 [B, Hq, Nq, n_splits, 2]; seqlens and bias as
+// for the prefill.
 hipError_t launch_decode_splitkv(const void* q, const void* k, const void* v, void* out,
-                                 float* lse, float* ws_o, float* ws_ml, const AttnShape& s,
+                                 float* lse, float* ws_o, float* ws_ml, const int* seqlens,
+                                 const void* bias, int bias_b, int bias_h, const AttnShape& s,
                                  float scale, bool causal, int n_splits, hipStream_t stream);
 
 }  // namespace fa

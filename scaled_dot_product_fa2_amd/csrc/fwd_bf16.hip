@@ -94,11 +94,12 @@ __device__ __forceinline__ void map_block(int n, int BH, int nqt, int& bh, int& 
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq,
-    int Hkv, int Nq, int Nk, int nqt, float scale, float scale_log2) {
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
+    int Hq, int Hkv, int Nq, int Nk_cap, int nqt, float scale, float scale_log2) {
   using C = FwdCfg<D>;
   constexpr int NC = D / 16;  // 16-element head-dim slices per QK product
   __shared__ __attribute__((aligned(1024))) uint16_t kl0[C::TILE];
@@ -114,14 +115,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   map_block(blockIdx.x, BH, nqt, bh, qt);
   const int b = bh / Hq, hq = bh - b * Hq;
   const int hkv = hq / (Hq / Hkv);
+  // keys of this batch element: all Nk_cap rows of K/V, or the first seqlens[b] (clamped)
+  const int Nk = seqlens ? min(max(seqlens[b], 0), Nk_cap) : Nk_cap;
   const int off = Nk - Nq;  // causal: key j visible to query i iff j <= i + off
   const int q_tile0 = qt * C::BR;
   const int qw0 = q_tile0 + wave * 32;  // first query row of this wave
   const int my_q = qw0 + l32;
 
   const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
-  const uint16_t* kg = K + (size_t)(b * Hkv + hkv) * Nk * D;
-  const uint16_t* vg = V + (size_t)(b * Hkv + hkv) * Nk * D;
+  const uint16_t* kg = K + (size_t)(b * Hkv + hkv) * Nk_cap * D;
+  const uint16_t* vg = V + (size_t)(b * Hkv + hkv) * Nk_cap * D;
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(Nq - 1, q_tile0 + C::BR - 1) + off + 1);
@@ -175,6 +178,48 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // Additive bias (bf16 [bias_b, bias_h, Nq, Nk_cap], batch and head dims broadcast when 1):
+  // the 32 values of a block that this lane's scores need, keys k0 + 32kb + 8g + 4h + 0..3,
+  // arrive as eight 8-byte loads through a resource covering this wave's 32 rows (rows past Nq
+  // read zero).  A block's bias, in score units (bias / scale), is the starting value of its
+  // score accumulators, so the registers that hold it are free again before the products of
+  // the block begin; they always hold the next block to be scored.
+  u32x2 bq[8];
+  const size_t b_slice = ((size_t)(bias_b == 1 ? 0 : b) * bias_h + (bias_h == 1 ? 0 : hq)) * Nq;
+  const __amdgpu_buffer_rsrc_t brs =
+      make_rsrc(BIAS ? bias + (b_slice + (size_t)min(qw0, Nq)) * Nk_cap : nullptr,
+                BIAS ? (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(32, Nq - qw0)) * Nk_cap * 2)
+                     : 0u);
+  const uint32_t b_lane = ((uint32_t)l32 * Nk_cap + 4u * h) * 2u;
+  const float inv_scale = 1.f / scale;
+  auto load_bias_into = [&](u32x2 (&dst)[8], int t) {
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dst[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                     brs, (int)(b_lane + (uint32_t)((32 * (i >> 2) + 8 * (i & 3)) * 2)),
+                     t * C::BC * 2, 0));
+    }
+  };
+  auto load_bias = [&](int t) { load_bias_into(bq, t); };
+  // bias of score register r of half kb, in score units
+  auto bias_of = [&](const u32x2 (&src)[8], int kb, int r) {
+    const uint32_t w = src[4 * kb + (r >> 2)][(r >> 1) & 1];
+    return __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16)) * inv_scale;
+  };
+  // zero, or the bias of the block whose scores come next
+  auto init_scores = [&](f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = bias_of(bq, kb, r);
+      } else {
+        s[kb] = f32x16{};
+      }
+    }
+  };
+
   auto active = [&](int t) { return (qw0 < Nq) && (!CAUSAL || t * C::BC <= qw0 + 31 + off); };
 
   // keys past Nk and, on diagonal blocks, keys after this row's last visible key -> -inf
@@ -196,8 +241,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   auto scores_lds = [&](const uint16_t* ks, f32x16 (&s)[2]) {
     u32x4 ka0 = *k_addr(ks, 0);
     u32x4 ka1 = *(k_addr(ks, 0) + 32 * D / 8);
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+    init_scores(s);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4 kn0 = ka0, kn1 = ka1;
@@ -256,6 +300,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // group 0's probabilities (only for blocks that need no mask).
   auto redo_block = [&](f32x16 (&s)[2], u32x4 (&pb)[4], int k0, float& mb) {
     scores_global(k0, s);
+    if constexpr (BIAS) {  // the bias registers already hold the next block: load this one again
+      u32x2 rb[8];
+      load_bias_into(rb, k0 / C::BC);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] += bias_of(rb, kb, r);
+    }
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -283,6 +335,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   int n_free = Nk / C::BC;
   if (CAUSAL) n_free = min(n_free, max(0, (q_tile0 + off + 1) / C::BC));
   n_free = min(n_free, n_tiles);
+  // With a bias the registers do not stretch to a lone pipelined step followed by the register
+  // copy below, so an odd last unmasked block goes through the in-order step.
+  if constexpr (BIAS) n_free &= ~1;
 
   // Steady-state step for an unmasked block t (scores in `s`): block t's exponentials are
   // interleaved instruction by instruction with the QK products of block t+1 (into `sn`), so
@@ -315,8 +370,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       kr[0][1] = *(k_addr(k_next, 0) + 32 * D / 8);
       kr[1][0] = *k_addr(k_next, 1);
       kr[1][1] = *(k_addr(k_next, 1) + 32 * D / 8);
-      sn[0] = f32x16{};
-      sn[1] = f32x16{};
+      init_scores(sn);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         if (c + 2 < NC) {
@@ -336,6 +390,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     }
     // an argument above kLazyLog2, or no reference yet: redo the block against its max
     if (wave_any(!(amax <= kLazyLog2) || m_run == -INFINITY)) redo_block(s, pb, t * C::BC, mb);
+    load_bias(t + 2);
 
     // Oᵀ += Vᵀ·Pᵀ, 16-key group by group (group g is operand pb[g]); while group g's products
     // run, group g+1's exponentials and group g's row sums are done.  V operands of group g+1
@@ -419,6 +474,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       for (int m4 = 0; m4 < 4; ++m4) oacc[db] = mfma32x32x16(vop[m4], pb[m4], oacc[db]);
     }
     if (t + 1 < n_tiles && active(t + 1)) scores_lds(k_next, s);
+    load_bias(t + 2);
   };
 
   // prologue: K[0], V[0], K[1], V[1] are requested together (all four buffers are free), the
@@ -426,6 +482,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // becomes the first reference.  Loads complete in issue order, so "at most 3·LPW loads
   // outstanding" means K[0] (and the Q rows loaded before it) have landed.
   if (n_tiles > 0) {
+    load_bias(0);
     issue_k(0, kl0);
     issue_v(0, vl0);
     issue_k(1, kl1);
@@ -438,7 +495,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     if (active(0)) {
       scores_lds(kl0, sA);
       if (n_free > 0) {
-        float mx = sA[0][0];
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -446,17 +503,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         m_run = pair32_max(mx);
       }
     }
+    load_bias(1);
   }
   int t = 0;
   for (; t + 1 < n_free; t += 2) {
     step(t, std::integral_constant<int, 0>{}, sA, sB);
     step(t + 1, std::integral_constant<int, 1>{}, sB, sA);
   }
-  if (t < n_free) {
-    step(t, std::integral_constant<int, 0>{}, sA, sB);
-    ++t;
+  if constexpr (!BIAS) {
+    if (t < n_free) {
+      step(t, std::integral_constant<int, 0>{}, sA, sB);
+      ++t;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sA[kb] = sB[kb];
+      for (int kb = 0; kb < 2; ++kb) sA[kb] = sB[kb];
+    }
   }
   for (; t < n_tiles; ++t) step_tail(t, sA);
 
@@ -478,28 +538,45 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 hipError_t launch(const void* q, const void* k, const void* v, void* out, float* lse,
+                  const int* seqlens, const void* bias, int bias_b, int bias_h,
                   const AttnShape& s, float scale, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int nqt = (s.Nq + C::BR - 1) / C::BR;
   const long long blocks = (long long)s.B * s.Hq * nqt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out,
-                     lse, s.Hq, s.Hkv, s.Nq, s.Nk, nqt, scale, scale * kLog2e);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BIAS>), dim3((unsigned)blocks), dim3(C::NT), 0,
+                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                     (uint16_t*)out, lse, seqlens, (const uint16_t*)bias, bias_b, bias_h, s.Hq,
+                     s.Hkv, s.Nq, s.Nk, nqt, scale, scale * kLog2e);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_b(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int* seqlens, const void* bias, int bias_b, int bias_h,
+                    const AttnShape& s, float scale, hipStream_t stream) {
+  return bias ? launch<D, CAUSAL, true>(q, k, v, out, lse, seqlens, bias, bias_b, bias_h, s, scale,
+                                        stream)
+              : launch<D, CAUSAL, false>(q, k, v, out, lse, seqlens, nullptr, 1, 1, s, scale,
+                                         stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int* seqlens, const void* bias, int bias_b, int bias_h,
                            const AttnShape& s, float scale, bool causal, hipStream_t stream) {
   if (s.d == 128)
-    return causal ? launch<128, true>(q, k, v, out, lse, s, scale, stream)
-                  : launch<128, false>(q, k, v, out, lse, s, scale, stream);
-  return causal ? launch<64, true>(q, k, v, out, lse, s, scale, stream)
-                : launch<64, false>(q, k, v, out, lse, s, scale, stream);
+    return causal ? launch_b<128, true>(q, k, v, out, lse, seqlens, bias, bias_b, bias_h, s,
+                                        scale, stream)
+                  : launch_b<128, false>(q, k, v, out, lse, seqlens, bias, bias_b, bias_h, s,
+                                         scale, stream);
+  return causal ? launch_b<64, true>(q, k, v, out, lse, seqlens, bias, bias_b, bias_h, s, scale,
+                                     stream)
+                : launch_b<64, false>(q, k, v, out, lse, seqlens, bias, bias_b, bias_h, s, scale,
+                                      stream);
 }
 
 }  // namespace fa

@@ -77,6 +77,41 @@ def draw_qkv(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
     return QKV(q=q, k=k, v=v, dtype=dtype)
 
 
+def draw_seqlens(seed: int, B: int, Nk: int, edges: bool = True) -> np.ndarray:
+    """Per-batch key lengths, int32 [B]: uniform in [1, Nk] from a seeded PCG64.  With ``edges``
+    the first entries become Nk, 0 and 1 (all keys, none, a single key), as far as B allows."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(1, max(Nk, 1) + 1, size=B).astype(np.int32) if Nk > 0 else np.zeros(B, np.int32)
+    if edges:
+        for i, val in enumerate((Nk, 0, min(1, Nk))[:B]):
+            L[i] = val
+    return L
+
+
+def draw_bias(seed: int, Bb: int, Hb: int, Nq: int, Nk: int, kind: str = "normal",
+              std: float = 1.0, masked_frac: float = 0.0) -> np.ndarray:
+    """An additive attention bias [Bb, Hb, Nq, Nk] as bfloat16 bits.
+
+    ``kind``: ``"normal"`` -- i.i.d. N(0, std^2) from a seeded PCG64; ``"alibi"`` -- a linear
+    distance penalty -slope_h * |i + (Nk - Nq) - j| with slopes 2^(-8 (h + 1) / Hb), the usual
+    position bias of decoder models.  ``masked_frac`` then sets that fraction of the entries,
+    chosen by the same generator, to -inf (a padding-style mask).
+    """
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        b = rng.standard_normal((Bb, Hb, Nq, Nk), dtype=np.float32) * np.float32(std)
+    elif kind == "alibi":
+        slopes = np.exp2(-8.0 * (np.arange(Hb) + 1) / Hb).astype(np.float32)
+        dist = np.abs(np.arange(Nq)[:, None] + (Nk - Nq) - np.arange(Nk)[None, :]).astype(np.float32)
+        b = np.broadcast_to(-slopes[None, :, None, None] * dist[None, None], (Bb, Hb, Nq, Nk))
+    else:
+        raise ValueError(f"unknown bias kind {kind!r}")
+    b = np.array(b, dtype=np.float32)
+    if masked_frac > 0:
+        b[rng.random(b.shape) < masked_frac] = -np.inf
+    return bf16_bits_from_f32(b)
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str

@@ -148,3 +148,77 @@ def test_ctypes_signatures_match_header(lib):
                 assert a is ctypes.c_float, (name, p)
             else:
                 assert p.startswith("int") and a is ctypes.c_int, (name, p)
+
+
+def _fwd_ex(lib, q=A16, k=A16, v=A16, o=A16, lse=None, seqlens=None, bias=None, bb=1, bh=1,
+            **kw):
+    a = {**GOOD, **kw}
+    return lib.attn_fwd_ex(q, k, v, o, lse, seqlens, bias, bb, bh, a["B"], a["Hq"], a["Hkv"],
+                           a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], None)
+
+
+def _dec_ex(lib, q=A16, k=A16, v=A16, o=A16, lse=None, ws=A16, ws_bytes=1 << 40, seqlens=None,
+            bias=None, bb=1, bh=1, S=2, **kw):
+    a = {**GOOD, **kw}
+    return lib.attn_decode_splitkv_ex(q, k, v, o, lse, ws, ws_bytes, seqlens, bias, bb, bh,
+                                      a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                                      a["scale"], a["causal"], S, None)
+
+
+@pytest.mark.parametrize("which", ["fwd", "dec"])
+def test_extras_validation(lib, which):
+    call = _fwd_ex if which == "fwd" else _dec_ex
+    base = dict(B=2, Hq=4, Hkv=2, Nq=8, Nk=12)
+    # the common checks come first, exactly as in the plain entry points
+    assert call(lib, **{**base, "d": 96}) == C["ATTN_ERR_HEADDIM"]
+    assert call(lib, q=None, **base) == C["ATTN_ERR_NULL"]
+    # bias dims: batch 1 or B, heads 1 or Hq; Nk a multiple of 4
+    for bb, bh in ((3, 1), (1, 2), (0, 1), (2, 5), (-1, 4)):
+        assert call(lib, bias=A16, bb=bb, bh=bh, **base) == C["ATTN_ERR_BIAS"], (bb, bh)
+    assert call(lib, bias=A16, bb=2, bh=4, **{**base, "Nk": 10}) == C["ATTN_ERR_BIAS"]
+    assert call(lib, bias=A16 + 8, bb=1, bh=1, **base) == C["ATTN_ERR_ALIGN"]
+    assert call(lib, seqlens=A16 + 2, **base) == C["ATTN_ERR_ALIGN"]
+    # without a bias its dims are not looked at, nor is Nk % 4
+    assert call(lib, bb=7, bh=9, **{**base, "d": 96, "Nk": 10}) == C["ATTN_ERR_HEADDIM"]
+    # empty problems succeed with any extras
+    assert call(lib, q=None, k=None, v=None, o=None, ws=None, seqlens=A16, bias=A16, bb=1, bh=1,
+                **{**base, "B": 0}) == C["ATTN_OK"]
+
+
+def test_decode_ex_workspace_and_splits(lib):
+    assert _dec_ex(lib, S=0) == C["ATTN_ERR_SPLITS"]
+    assert _dec_ex(lib, ws=None) == C["ATTN_ERR_WORKSPACE"]
+    need = lib.attn_decode_workspace_bytes(1, 4, 8, 128, 2)
+    assert _dec_ex(lib, ws_bytes=need - 1) == C["ATTN_ERR_WORKSPACE"]
+
+
+def test_num_splits(lib):
+    # 8 x 8 KV heads, 4 query rows each: 64 workgroups per split -> 16 splits for ~1024
+    assert lib.attn_decode_num_splits(8, 32, 8, 1, 8192) == 16
+    # few workgroups per split, but no split shorter than 256 keys
+    assert lib.attn_decode_num_splits(1, 8, 8, 1, 512) == 2
+    assert lib.attn_decode_num_splits(1, 8, 8, 1, 100) == 1
+    assert lib.attn_decode_num_splits(1, 1, 1, 1, 1 << 24) == 256  # capped
+    assert lib.attn_decode_num_splits(64, 64, 64, 16, 8192) == 1   # the grid is full already
+    assert lib.attn_decode_num_splits(0, 8, 8, 1, 512) == 1
+    assert lib.attn_decode_num_splits(1, 6, 4, 1, 512) == 1        # invalid GQA
+
+
+def test_forward_workspace_and_routing(lib):
+    # prefill route from 32 query rows on: no workspace
+    assert lib.attn_forward_workspace_bytes(2, 16, 16, 32, 4096, 128) == 0
+    s = lib.attn_decode_num_splits(8, 32, 8, 31, 8192)
+    assert lib.attn_forward_workspace_bytes(8, 32, 8, 31, 8192, 128) == \
+        lib.attn_decode_workspace_bytes(8, 32, 31, 128, s)
+
+    def fwd(ws=A16, ws_bytes=1 << 40, **kw):
+        a = {**GOOD, **kw}
+        return lib.attn_forward(A16, A16, A16, A16, None, ws, ws_bytes, None, None, 1, 1, a["B"],
+                                a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                a["causal"], None)
+
+    # below 32 rows the split-KV path runs, so its workspace is required
+    assert fwd(ws=None, Nq=8) == C["ATTN_ERR_WORKSPACE"]
+    assert fwd(ws_bytes=1, Nq=31, Nk=64) == C["ATTN_ERR_WORKSPACE"]
+    assert fwd(ws=None, Nq=8, d=96) == C["ATTN_ERR_HEADDIM"]
+    assert fwd(ws=None, B=0) == C["ATTN_OK"]
