@@ -19,7 +19,8 @@ before the timed region so that host-side overhead cannot leave the GPU idle ins
   roofline   the prefill kernel against the bf16 dense MFMA peak (and decode against 8 TB/s);
   cpu_baseline  the CPU fp64 oracle timed on a bounded sample of the prefill workload.
 
-Options: --sweep prints one extra line per prefill/decode workload; --only runs a single
+Options: --sweep prints one extra line per prefill/decode workload; --extras prints one line per
+variant with per-batch key lengths or an additive bias (see ``extras``); --only runs a single
 workload for profiler runs; --copy-bytes runs a plain device copy for counter calibration.
 """
 from __future__ import annotations
@@ -91,13 +92,14 @@ def ensure_built():
 
 
 class Prefill:
-    def __init__(self, w, torch, fa, I):
+    def __init__(self, w, torch, fa, I, seqlens_k=None, bias=None):
         self.w, self.torch, self.fa = w, torch, fa
         x = w.draw()
         self.q, self.k, self.v = (I.to_device(a, "bf16") for a in (x.q, x.k, x.v))
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
-        self.call = fa.prepare_fwd(self.q, self.k, self.v, self.out, self.lse, causal=w.causal)
+        self.call = fa.prepare_fwd(self.q, self.k, self.v, self.out, self.lse, causal=w.causal,
+                                   seqlens_k=seqlens_k, bias=bias)
 
     def __call__(self, i):
         self.call()
@@ -107,7 +109,7 @@ class Prefill:
 
 
 class Decode:
-    def __init__(self, w, torch, fa, I, kv_sets):
+    def __init__(self, w, torch, fa, I, kv_sets, seqlens_k=None, bias=None):
         self.w, self.torch, self.fa = w, torch, fa
         self.kv = []
         for s in range(len(kv_sets)):
@@ -119,7 +121,8 @@ class Decode:
         need = fa.attn_decode_workspace_bytes(w.B, w.Hq, w.Nq, w.d, w.n_splits)
         self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         self.calls = [fa.prepare_decode(self.q, k, v, w.n_splits, self.out, self.lse, self.ws,
-                                        causal=w.causal) for k, v in self.kv]
+                                        causal=w.causal, seqlens_k=seqlens_k, bias=bias)
+                      for k, v in self.kv]
 
     def __call__(self, i):
         self.calls[i % len(self.calls)]()
@@ -205,6 +208,70 @@ def cpu_baseline(w, target_s: float):
                       f"{cores} threads"}
 
 
+def visible_pairs(Nq, L, causal):
+    """(query, key) pairs a row block attends to with L keys, causal mask aligned to the end."""
+    if not causal:
+        return Nq * L
+    return sum(max(0, min(L, i + L - Nq + 1)) for i in range(Nq))
+
+
+def extras(torch, fab, I, W, steps, warmup, kv):
+    """One line per variant with the optional inputs, each timed like the main parts:
+      * prefill with a bias shared by the batch ([1, H, N, N], an ALiBi-style distance penalty)
+        and with a bias per (batch, head) ([B, H, N, N], which must stream from HBM);
+      * prefill with a length mix (per-batch key counts uniform in [1, N]); its TFLOPS count
+        only the visible (query, key) pairs of each element;
+      * decode (Nq=1 and Nq=4) with a length mix over the 8192-key capacity (GB/s over the K/V
+        rows that exist) and with a per-head bias [1, Hq, Nq, Nk] (its bytes counted)."""
+    w = W[HEADLINE]
+    rows = []
+
+    def prefill_line(name, part, flops, extra_bytes):
+        _, (ms,) = time_steps(torch, [part], steps, warmup)
+        tf = flops / (ms * 1e-3) / 1e12
+        line = {"extra": name, "workload": w.name, "mean_ms": round(ms, 5), "TFLOPS": round(tf, 1),
+                "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+        if extra_bytes:
+            line["bias_bytes"] = extra_bytes
+            line["bias_GBps"] = round(extra_bytes / (ms * 1e-3) / 1e9, 1)
+        rows.append(line)
+        print(json.dumps(line), flush=True)
+
+    for bb, kind in ((1, "alibi"), (w.B, "normal")):
+        bits = I.draw_bias(1000 + bb, bb, w.Hq, w.Nq, w.Nk, kind)
+        bias = I.to_device(bits, "bf16")
+        prefill_line(f"bias_{bb}x{w.Hq}_{kind}", Prefill(w, torch, fab, I, bias=bias), w.flops(),
+                     bits.size * 2)
+        del bias
+    L = I.draw_seqlens(1010, w.B, w.Nk, edges=False)
+    flops = sum(4.0 * w.Hq * w.d * visible_pairs(w.Nq, int(l), w.causal) for l in L)
+    lens = torch.as_tensor(L, device="cuda")
+    prefill_line(f"varlen_{'_'.join(str(int(x)) for x in L)}",
+                 Prefill(w, torch, fab, I, seqlens_k=lens), flops, 0)
+
+    for name in DECODE:
+        wd = W[name]
+        L = I.draw_seqlens(1020, wd.B, wd.Nk, edges=False)
+        lens = torch.as_tensor(L, device="cuda")
+        bits = I.draw_bias(1030, 1, wd.Hq, wd.Nq, wd.Nk, "alibi")
+        bias = I.to_device(bits, "bf16")
+        qo = 2 * wd.B * wd.Hq * wd.Nq * wd.d * 2 + wd.B * wd.Hq * wd.Nq * 4
+        for tag, kw, nbytes in (
+                ("varlen", {"seqlens_k": lens}, 2 * int(L.sum()) * wd.Hkv * wd.d * 2 + qo),
+                ("bias", {"bias": bias}, algorithmic_bytes(wd) + bits.size * 2)):
+            part = Decode(wd, torch, fab, I, kv, **kw)
+            _, (ms,) = time_steps(torch, [part], steps, warmup)
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            line = {"extra": tag, "workload": name, "mean_ms": round(ms, 5),
+                    "algorithmic_bytes": nbytes, "GBps": round(gbps, 1),
+                    "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+            if tag == "varlen":
+                line["seqlens_k"] = [int(x) for x in L]
+            rows.append(line)
+            print(json.dumps(line), flush=True)
+    return rows
+
+
 def roofline_mfma(flops, ms, traffic):
     achieved = flops / (ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -224,6 +291,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sweep", action="store_true", help="also print one line per workload")
+    ap.add_argument("--extras", action="store_true",
+                    help="also print one line per key-length / bias variant")
     ap.add_argument("--only", default=None, help="run only this workload (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -309,6 +378,9 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+    if args.extras:
+        extras(torch, fab, I, W, args.steps, args.warmup, kv)
 
     if args.sweep:
         for name, wk in W.items():

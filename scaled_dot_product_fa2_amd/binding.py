@@ -279,36 +279,48 @@ def attn_forward(q, k, v, causal: bool = True, scale: float = 0.0, seqlens_k=Non
     return out, lse, workspace
 
 
-def prepare_fwd(q, k, v, out, lse=None, causal: bool = True, scale: float = 0.0):
-    """A zero-argument callable that enqueues ``attn_fwd`` with these tensors on the current
-    stream, with every argument marshalled once up front (for timing loops)."""
+def prepare_fwd(q, k, v, out, lse=None, causal: bool = True, scale: float = 0.0, seqlens_k=None,
+                bias=None):
+    """A zero-argument callable that enqueues ``attn_fwd`` (``attn_fwd_ex`` when extras are
+    given) with these tensors on the current stream, with every argument marshalled once up
+    front (for timing loops)."""
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
-    fn = load().attn_fwd
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, float(scale),
-            int(bool(causal)), _stream(q.device))
+    tail = (B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(q.device))
+    if seqlens_k is None and bias is None:
+        fn, name = load().attn_fwd, "attn_fwd"
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)) + tail
+    else:
+        fn, name = load().attn_fwd_ex, "attn_fwd_ex"
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                *_extras(q, B, Hq, Nq, Nk, seqlens_k, bias)) + tail
 
     def call():
         rc = fn(*args)
         if rc != ATTN_OK:
-            _check_rc(rc, "attn_fwd")
+            _check_rc(rc, name)
     return call
 
 
 def prepare_decode(q, k, v, n_splits: int, out, lse, workspace, causal: bool = True,
-                   scale: float = 0.0):
-    """The same for ``attn_decode_splitkv``."""
+                   scale: float = 0.0, seqlens_k=None, bias=None):
+    """The same for ``attn_decode_splitkv`` (``attn_decode_splitkv_ex`` with extras)."""
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
-    fn = load().attn_decode_splitkv
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d, float(scale),
-            int(bool(causal)), int(n_splits), _stream(q.device))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    tail = (B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(n_splits),
+            _stream(q.device))
+    if seqlens_k is None and bias is None:
+        fn, name, args = load().attn_decode_splitkv, "attn_decode_splitkv", head + tail
+    else:
+        fn, name = load().attn_decode_splitkv_ex, "attn_decode_splitkv_ex"
+        args = head + tuple(_extras(q, B, Hq, Nq, Nk, seqlens_k, bias)) + tail
 
     def call():
         rc = fn(*args)
         if rc != ATTN_OK:
-            _check_rc(rc, "attn_decode_splitkv")
+            _check_rc(rc, name)
     return call

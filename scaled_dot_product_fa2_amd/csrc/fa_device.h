@@ -81,6 +81,10 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, u32x4 b, f32x16 c) {
 // probabilities stay below 2^kLazyLog2 and the accumulator is rarely rescaled.  O and l always
 // share the same reference max, so the final O / l is unchanged.
 constexpr float kLazyLog2 = 8.0f;
+// Largest block-to-block rise of the max (log2 units) that a rescale may absorb in registers
+// from probabilities already computed against the old reference: 2^120 is still finite in fp32
+// and bf16.
+constexpr float kShiftMax = 120.0f;
 
 // Buffer resource covering `bytes` bytes from `base` (raw addressing, no stride).  Buffer loads
 // through it read zero past the end, which is how K/V rows beyond the sequence are filled.
@@ -113,5 +117,6 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 // 64 lanes of the wave vote: true when the predicate holds in any active lane.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+__device__ __forceinline__ bool wave_all(bool p) { return !wave_any(!p); }
 
 }  // namespace fa

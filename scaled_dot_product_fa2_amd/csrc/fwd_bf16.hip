@@ -106,6 +106,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t kl1[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vl0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vl1[C::TILE];
+  // bias: each wave's 32 rows x BC keys, one buffer per wave (16 KB in all, so that two
+  // workgroups still fit a CU's 160 KB)
+  __shared__ __attribute__((aligned(1024))) uint16_t bl[BIAS ? 4 * 32 * C::BC : 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -178,45 +181,69 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Additive bias (bf16 [bias_b, bias_h, Nq, Nk_cap], batch and head dims broadcast when 1):
-  // the 32 values of a block that this lane's scores need, keys k0 + 32kb + 8g + 4h + 0..3,
-  // arrive as eight 8-byte loads through a resource covering this wave's 32 rows (rows past Nq
-  // read zero).  A block's bias, in score units (bias / scale), is the starting value of its
-  // score accumulators, so the registers that hold it are free again before the products of
-  // the block begin; they always hold the next block to be scored.
-  u32x2 bq[8];
+  // Additive bias (bf16 [bias_b, bias_h, Nq, Nk_cap], batch and head dims broadcast when 1), in
+  // score units (bias / scale).  A block's bias is the starting value of its score accumulators.
+  // Each wave copies its own 32 rows x BC keys of bias into its LDS slice (four 1 KB copies of
+  // eight 128-byte rows, coalesced) through a resource covering its rows (rows past Nq read
+  // zero); the copy of block x+1 is requested once block x has been read out, and as a wave only
+  // reads its own slice no barrier is involved.  Slot p of row 8i+j holds 16-byte chunk
+  // p ^ f(i, j), f = (j >> 1) | ((i & 1) << 2): the 8-byte reads of one chunk by the 32 rows then
+  // fall on distinct bank pairs within each half of the 64 banks.  The rarely taken path that
+  // recomputes a block reads its bias from global memory instead.
   const size_t b_slice = ((size_t)(bias_b == 1 ? 0 : b) * bias_h + (bias_h == 1 ? 0 : hq)) * Nq;
   const __amdgpu_buffer_rsrc_t brs =
       make_rsrc(BIAS ? bias + (b_slice + (size_t)min(qw0, Nq)) * Nk_cap : nullptr,
                 BIAS ? (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(32, Nq - qw0)) * Nk_cap * 2)
                      : 0u);
-  const uint32_t b_lane = ((uint32_t)l32 * Nk_cap + 4u * h) * 2u;
   const float inv_scale = 1.f / scale;
-  auto load_bias_into = [&](u32x2 (&dst)[8], int t) {
+  const float inv_scale_log2 = 1.f / scale_log2;
+  uint16_t* const bw = bl + (BIAS ? wave * 32 * C::BC : 0);
+  const int bj = lane >> 3, bp = lane & 7;
+  const uint32_t b_row = (uint32_t)bj * Nk_cap * 2, b_cw = (uint32_t)(bp ^ (bj >> 1)) << 4;
+  auto issue_bias = [&](int t) {
     if constexpr (BIAS) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dst[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                     brs, (int)(b_lane + (uint32_t)((32 * (i >> 2) + 8 * (i & 3)) * 2)),
-                     t * C::BC * 2, 0));
+      for (int i = 0; i < 4; ++i)
+        load_lds_16(brs, bw + i * 8 * C::BC, b_row + (b_cw ^ ((i & 1) << 6)),
+                    (uint32_t)(8 * i) * Nk_cap * 2 + (uint32_t)t * (C::BC * 2));
     }
   };
-  auto load_bias = [&](int t) { load_bias_into(bq, t); };
-  // bias of score register r of half kb, in score units
-  auto bias_of = [&](const u32x2 (&src)[8], int kb, int r) {
-    const uint32_t w = src[4 * kb + (r >> 2)][(r >> 1) & 1];
-    return __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16)) * inv_scale;
+  // this lane's 8-byte read of logical chunk c (keys 8c .. 8c+7, half h) is b_rd ^ (16 c)
+  const uint32_t b_rd = (uint32_t)l32 * (C::BC * 2) +
+                        ((uint32_t)(((l32 & 7) >> 1) | (((l32 >> 3) & 1) << 2)) << 4) + 8u * h;
+  auto bias_val = [&](uint32_t w, int odd) {
+    return __uint_as_float(odd ? (w & 0xffff0000u) : (w << 16)) * inv_scale;
   };
-  // zero, or the bias of the block whose scores come next
+  // zero, or the bias of the block whose scores come next (from this wave's LDS slice)
   auto init_scores = [&](f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (BIAS) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = bias_of(bq, kb, r);
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = *(const u32x2*)((const char*)bw + (b_rd ^ (uint32_t)((4 * kb + g) << 4)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kb][4 * g + e] = bias_val(w[e >> 1], e & 1);
+        }
       } else {
         s[kb] = f32x16{};
       }
+    }
+  };
+  // the same values of block t straight from global memory (eight 8-byte loads per lane)
+  const uint32_t b_lane = ((uint32_t)l32 * Nk_cap + 4u * h) * 2u;
+  auto add_bias_global = [&](f32x16 (&s)[2], int t) {
+    if constexpr (BIAS) {
+      u32x2 w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                   brs, (int)(b_lane + (uint32_t)((32 * (i >> 2) + 8 * (i & 3)) * 2)),
+                   t * C::BC * 2, 0));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] += bias_val(w[4 * kb + (r >> 2)][(r >> 1) & 1], r & 1);
     }
   };
 
@@ -300,14 +327,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // group 0's probabilities (only for blocks that need no mask).
   auto redo_block = [&](f32x16 (&s)[2], u32x4 (&pb)[4], int k0, float& mb) {
     scores_global(k0, s);
-    if constexpr (BIAS) {  // the bias registers already hold the next block: load this one again
-      u32x2 rb[8];
-      load_bias_into(rb, k0 / C::BC);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] += bias_of(rb, kb, r);
-    }
+    add_bias_global(s, k0 / C::BC);  // the LDS slice already holds the next block
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -328,6 +348,26 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     for (int j = 0; j < 8; j += 2) exp_pair(s, pb, j);
   };
 
+  // The block's arguments exceed the bound by at most kShiftMax: move the reference up by the
+  // block's own largest argument in registers.  Arguments not yet exponentiated drop by that
+  // amount, the probabilities already taken (group 0) and O, l scale by 2^-shift; rows within
+  // the bound keep their reference.  Group 0's probabilities are at most 2^kShiftMax, finite.
+  auto shift_block = [&](f32x16 (&s)[2], u32x4 (&pb)[4], float bmax) {
+    const float sh = bmax > kLazyLog2 ? bmax : 0.f;
+    const float alpha = fast_exp2(-sh);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    l_run *= alpha;
+    m_run += sh * inv_scale_log2;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j < 8) s[j >> 4][j & 15] *= alpha;
+      else s[j >> 4][j & 15] -= sh;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) pb[0][j >> 1] = pack_bf16x2(s[0][j], s[0][j + 1]);
+  };
+
   f32x16 sA[2], sB[2];
 
   // Blocks [0, n_free) need no mask for any wave of the workgroup: every key is below Nk and,
@@ -335,9 +375,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   int n_free = Nk / C::BC;
   if (CAUSAL) n_free = min(n_free, max(0, (q_tile0 + off + 1) / C::BC));
   n_free = min(n_free, n_tiles);
-  // With a bias the registers do not stretch to a lone pipelined step followed by the register
-  // copy below, so an odd last unmasked block goes through the in-order step.
-  if constexpr (BIAS) n_free &= ~1;
 
   // Steady-state step for an unmasked block t (scores in `s`): block t's exponentials are
   // interleaved instruction by instruction with the QK products of block t+1 (into `sn`), so
@@ -388,9 +425,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         }
       }
     }
-    // an argument above kLazyLog2, or no reference yet: redo the block against its max
-    if (wave_any(!(amax <= kLazyLog2) || m_run == -INFINITY)) redo_block(s, pb, t * C::BC, mb);
-    load_bias(t + 2);
+    // an argument above kLazyLog2: shift the reference in registers, or, when the jump is
+    // larger than kShiftMax or there is no reference yet, redo the block against its max
+    if (wave_any(!(amax <= kLazyLog2) || m_run == -INFINITY)) {
+      const float bmax = pair32_max(amax);
+      const bool fast = wave_all(bmax <= kShiftMax && m_run != -INFINITY);
+      // (not an if / else: the two paths' register demands would then add up)
+      shift_block(s, pb, fast ? bmax : 0.f);  // a no-op when the block is redone
+      if (!fast) redo_block(s, pb, t * C::BC, mb);
+    }
+    if (t + 2 < n_tiles) issue_bias(t + 2);  // block t+1's bias has been read out
 
     // Oᵀ += Vᵀ·Pᵀ, 16-key group by group (group g is operand pb[g]); while group g's products
     // run, group g+1's exponentials and group g's row sums are done.  V operands of group g+1
@@ -474,7 +518,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       for (int m4 = 0; m4 < 4; ++m4) oacc[db] = mfma32x32x16(vop[m4], pb[m4], oacc[db]);
     }
     if (t + 1 < n_tiles && active(t + 1)) scores_lds(k_next, s);
-    load_bias(t + 2);
+    if (t + 2 < n_tiles) issue_bias(t + 2);
   };
 
   // prologue: K[0], V[0], K[1], V[1] are requested together (all four buffers are free), the
@@ -482,7 +526,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   // becomes the first reference.  Loads complete in issue order, so "at most 3·LPW loads
   // outstanding" means K[0] (and the Q rows loaded before it) have landed.
   if (n_tiles > 0) {
-    load_bias(0);
+    issue_bias(0);  // before K[0], so the wait below covers it
     issue_k(0, kl0);
     issue_v(0, vl0);
     issue_k(1, kl1);
@@ -503,20 +547,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         m_run = pair32_max(mx);
       }
     }
-    load_bias(1);
+    if (n_tiles > 1) issue_bias(1);
   }
   int t = 0;
   for (; t + 1 < n_free; t += 2) {
     step(t, std::integral_constant<int, 0>{}, sA, sB);
     step(t + 1, std::integral_constant<int, 1>{}, sB, sA);
   }
-  if constexpr (!BIAS) {
-    if (t < n_free) {
-      step(t, std::integral_constant<int, 0>{}, sA, sB);
-      ++t;
+  if (t < n_free) {
+    step(t, std::integral_constant<int, 0>{}, sA, sB);
+    ++t;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sA[kb] = sB[kb];
-    }
+    for (int kb = 0; kb < 2; ++kb) sA[kb] = sB[kb];
   }
   for (; t < n_tiles; ++t) step_tail(t, sA);
 

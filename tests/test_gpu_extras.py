@@ -139,6 +139,22 @@ def test_prefill_bias_and_varlen_together():
                 what=f"bias+varlen causal={causal}")
 
 
+@pytest.mark.parametrize("slope", [0.02, 0.5, 2.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_bias_rising_max(slope, causal):
+    # a bias rising along the keys lifts every row's max block after block: by 64*slope per
+    # 64-key block (natural units), i.e. below the lazy bound, within the in-register shift, and
+    # beyond it (the block is then recomputed from K)
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 256, 640, 128
+    ramp = (slope * np.arange(Nk, dtype=np.float32))[None, None, None, :]
+    rows = np.linspace(0.0, 3.0, Nq, dtype=np.float32)[None, None, :, None]
+    bits = I.bf16_bits_from_f32(np.broadcast_to(ramp + rows, (1, 1, Nq, Nk)))
+    out, lse, O_ref, lse_ref = _prefill(B, Hq, Hkv, Nq, Nk, d, causal, 660, bias_bits=bits)
+    compare(out, lse, O_ref, lse_ref, BF16_MAX_ABS, BF16_MEAN_ABS,
+            lse_tol=1e-3 + 4 * 2.0**-23 * float(np.abs(lse_ref[np.isfinite(lse_ref)]).max()),
+            what=f"rising bias slope={slope} causal={causal}")
+
+
 def test_prefill_bias_masked_rows():
     # rows whose every key is masked by a -inf bias: output 0 and lse -inf, like Nk = 0
     B, Hq, Hkv, Nq, Nk, d = 1, 2, 2, 100, 128, 128
