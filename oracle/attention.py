@@ -36,6 +36,12 @@ Readings where the pages are silent (each applied identically everywhere):
   does (section 1 of the PyTorch page writes masked positions as -inf), so a row whose every
   key is masked this way is a row with no visible key.
 
+* Backward (``attention_backward_fp64``): not on the pages.  The gradients of the scalar
+  L = Σ dO ∘ O are the chain rule through the same five steps, written out as the definition:
+  dV = Pᵀ·dO, dP = dO·Vᵀ, dS = P ∘ (dP − Σ_k P_ik dP_ik) (the softmax Jacobian), dQ = scale·dS·K,
+  dK = scale·dSᵀ·Q; K/V heads shared by several query heads (GQA) receive the sum over those
+  heads.  Masked positions have P = 0 and pass no gradient.
+
 All arithmetic is numpy float64; the matrix product (``@``) is the only library primitive.
 """
 from __future__ import annotations
@@ -336,3 +342,43 @@ def flash2_tiled_fp64(q, k, v, scale: float, causal: bool, Br: int, Bc: int,
                                               where=ok[:, None])
                 lse[b, hq, i0:i1] = _row_lse(m, l)
     return out, lse
+
+
+def _softmax_backward(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
+    """Gradient w.r.t. the scores of a row softmax: dS_ij = P_ij (dP_ij − Σ_k P_ik dP_ik)."""
+    return p * (dp - (p * dp).sum(axis=1, keepdims=True))
+
+
+def _accumulate(acc: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """Sum over the query heads that share one K/V head."""
+    return acc + x
+
+
+def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool):
+    """(dq [B,Hq,Nq,d], dk [B,Hkv,Nk,d], dv [B,Hkv,Nk,d]): the gradients of L = Σ dout ∘ O for
+    O = softmax(scale·q·kᵀ + causal mask)·v, in fp64, from the definition (see the module
+    docstring).  Small and medium inputs only: every (batch, head) keeps its [Nq, Nk] matrices."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError(f"dout must have the shape of q {q.shape}, got {dout.shape}")
+    scale = _resolve_scale(scale, d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rows = np.arange(Nq)
+    vis = visible_mask(rows, Nq, Nk, causal)
+    for b in range(B):
+        for hq in range(Hq):
+            hkv = _kv_head(hq, Hq, Hkv)
+            kh, vh, qh, doh = k[b, hkv], v[b, hkv], q[b, hq], dout[b, hq]
+            p, _, _ = _masked_softmax(_scores(qh, kh, scale), vis)
+            dp = doh @ vh.T
+            ds = _softmax_backward(p, dp)
+            dq[b, hq] = scale * (ds @ kh)
+            dk[b, hkv] = _accumulate(dk[b, hkv], scale * (ds.T @ qh))
+            dv[b, hkv] = _accumulate(dv[b, hkv], p.T @ doh)
+    return dq, dk, dv

@@ -493,6 +493,70 @@ def pin_bias_neg_inf_is_mask():
     assert np.all(l_s[:, 1, 2] == 0.0) and np.all(m_s[:, 1, 2] == -np.inf), "all -inf split"
 
 
+# ---- backward ------------------------------------------------------------------------------
+
+def _loss(q, k, v, g, scale, causal):
+    O, _ = A.attention_fp64(q, k, v, scale, causal)
+    return float((O * g).sum())
+
+
+def pin_bwd_finite_differences():
+    """Every gradient element against a central difference of L = Σ g ∘ O through the forward
+    oracle (itself pinned above), with GQA, causal and non-causal, rows without keys."""
+    h = 1e-6
+    for causal, (Nq, Nk) in ((False, (4, 5)), (True, (4, 5)), (True, (5, 3))):
+        B, Hq, Hkv, d = 1, 2, 1, 3
+        q, k, v = _rand(700, B, Hq, Nq, d), _rand(701, B, Hkv, Nk, d), _rand(702, B, Hkv, Nk, d)
+        g = _rand(703, B, Hq, Nq, d)
+        grads = A.attention_backward_fp64(q, k, v, g, 0.7, causal)
+        for t, (x, gx) in enumerate(zip((q, k, v), grads)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[t], args_m[t] = xp, xm
+                num[idx] = (_loss(*args_p, g, 0.7, causal) - _loss(*args_m, g, 0.7, causal)) / (2 * h)
+            _close(gx, num, 1e-7, f"finite differences causal={causal} tensor {'qkv'[t]}")
+
+
+def pin_bwd_shift_invariances():
+    """Shifting every key by c leaves O unchanged (a row-constant score change), so Σ_j dK_j = 0;
+    shifting every value by c shifts O by c on rows with a visible key, so Σ_j dV_j = Σ dO over
+    those rows; scaling q and scaling k by α change the scores alike, so Σ q∘dq = Σ k∘dk."""
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 6, 9, 5
+    for causal, Nq_ in ((False, Nq), (True, Nq), (True, 12)):
+        q, k, v = _rand(710, B, Hq, Nq_, d), _rand(711, B, Hkv, Nk, d), _rand(712, B, Hkv, Nk, d)
+        g = _rand(713, B, Hq, Nq_, d)
+        dq, dk, dv = A.attention_backward_fp64(q, k, v, g, 0.4, causal)
+        _close(dk.sum(axis=2), np.zeros((B, Hkv, d)), 1e-12, "sum of dK")
+        has = _tril_visible(Nq_, Nk, causal).any(axis=1)
+        G = Hq // Hkv
+        want = g[:, :, has].sum(axis=2).reshape(B, Hkv, G, d).sum(axis=2)
+        _close(dv.sum(axis=2), want, 1e-12, "sum of dV")
+        lhs = (q * dq).reshape(B, Hkv, G, Nq_, d).sum(axis=(2, 3, 4))
+        rhs = (k * dk).sum(axis=(2, 3))
+        _close(lhs, rhs, 1e-12, "q.dq = k.dk")
+
+
+def pin_bwd_gqa_equals_repeated_heads():
+    """With K/V shared by G query heads, dK and dV are the sums over those heads of the
+    gradients computed with K/V repeated per head (plain multi-head attention)."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 6, 2, 5, 7, 4
+    q, k, v = _rand(720, B, Hq, Nq, d), _rand(721, B, Hkv, Nk, d), _rand(722, B, Hkv, Nk, d)
+    g = _rand(723, B, Hq, Nq, d)
+    G = Hq // Hkv
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    for causal in (False, True):
+        dq, dk, dv = A.attention_backward_fp64(q, k, v, g, 0.5, causal)
+        dq1, dk1, dv1 = A.attention_backward_fp64(q, kr, vr, g, 0.5, causal)
+        _close(dq, dq1, 1e-12, "GQA dq")
+        _close(dk, dk1.reshape(B, Hkv, G, Nk, d).sum(axis=2), 1e-12, "GQA dk")
+        _close(dv, dv1.reshape(B, Hkv, G, Nk, d).sum(axis=2), 1e-12, "GQA dv")
+
+
 ALL_PINS = [
     pin_probs_rows_sum_to_one,
     pin_constant_values,
@@ -519,4 +583,7 @@ ALL_PINS = [
     pin_bias_row_shift,
     pin_bias_rank_one_is_extra_head_dim,
     pin_bias_neg_inf_is_mask,
+    pin_bwd_finite_differences,
+    pin_bwd_shift_invariances,
+    pin_bwd_gqa_equals_repeated_heads,
 ]

@@ -112,6 +112,13 @@ MUTANTS = {
     "bias_heads_reversed": ("_bias_view", _bias_transposed_heads),
     "seqlens_ignored": ("_key_lengths", _key_lengths_capacity),
     "seqlens_off_by_one": ("_key_lengths", _key_lengths_minus_one),
+    "bwd_softmax_not_centred": ("_softmax_backward", lambda p, dp: p * dp),
+    "bwd_softmax_sign": ("_softmax_backward",
+                         lambda p, dp: p * ((p * dp).sum(axis=1, keepdims=True) - dp)),
+    "bwd_softmax_centred_on_mean": ("_softmax_backward",
+                                    lambda p, dp: p * (dp - dp.mean(axis=1, keepdims=True))),
+    "bwd_gqa_last_head_only": ("_accumulate", lambda acc, x: x),
+    "bwd_gqa_average": ("_accumulate", lambda acc, x: 0.5 * (acc + x)),
 }
 
 _ORIG = {name: getattr(A, name) for name, _ in MUTANTS.values()}
