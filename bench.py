@@ -20,8 +20,10 @@ before the timed region so that host-side overhead cannot leave the GPU idle ins
   cpu_baseline  the CPU fp64 oracle timed on a bounded sample of the prefill workload.
 
 Options: --sweep prints one extra line per prefill/decode workload; --extras prints one line per
-variant with per-batch key lengths or an additive bias (see ``extras``); --only runs a single
-workload for profiler runs; --copy-bytes runs a plain device copy for counter calibration.
+variant with per-batch key lengths or an additive bias (see ``extras``); --bwd prints one line per
+backward workload (see ``backward``); --only runs a single workload for profiler runs (a name
+ending in ":bwd" runs its backward); --copy-bytes runs a plain device copy for counter
+calibration.
 """
 from __future__ import annotations
 
@@ -208,6 +210,50 @@ def cpu_baseline(w, target_s: float):
                       f"{cores} threads"}
 
 
+class Backward:
+    """attn_bwd on a workload's inputs, after one forward call that provides out and LSE."""
+
+    def __init__(self, w, torch, fa, I):
+        x = w.draw()
+        self.q, self.k, self.v = (I.to_device(a, "bf16") for a in (x.q, x.k, x.v))
+        self.dout = I.to_device(I.draw_grad(w.seed + 1, (w.B, w.Hq, w.Nq, w.d)), "bf16")
+        self.out, self.lse = fa.attn_fwd(self.q, self.k, self.v, causal=w.causal)
+        self.dq, self.dk, self.dv = (torch.empty_like(t) for t in (self.q, self.k, self.v))
+        ws = torch.empty(max(fa.attn_bwd_workspace_bytes(w.B, w.Hq, w.Nq), 16), dtype=torch.uint8,
+                         device="cuda")
+        self.ws = ws
+        self.call = fa.prepare_bwd(self.q, self.k, self.v, self.out, self.lse, self.dout, self.dq,
+                                   self.dk, self.dv, ws, causal=w.causal)
+
+    def __call__(self, i):
+        self.call()
+
+
+def bwd_flops(w):
+    """Backward FLOP convention: the five products of the gradient (dV, dP, dQ, dK and the
+    recomputed S) at 2*Nq*Nk*d each, i.e. 2.5x the forward's, halved when causal; the kernels
+    recompute S and dP once more (seven products executed)."""
+    return 2.5 * w.flops()
+
+
+def backward(torch, fab, I, W, steps, warmup, names=("prefill_causal_b2h16n2048",
+                                                      "sweep_n4096_b4_causal",
+                                                      "long_causal_b1h8n16384")):
+    rows = []
+    for name in names:
+        w = W[name]
+        part = Backward(w, torch, fab, I)
+        _, (ms,) = time_steps(torch, [part], steps, warmup)
+        tf = bwd_flops(w) / (ms * 1e-3) / 1e12
+        line = {"backward": name, "mean_ms": round(ms, 5), "TFLOPS": round(tf, 1),
+                "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+        rows.append(line)
+        print(json.dumps(line), flush=True)
+        del part
+        torch.cuda.empty_cache()
+    return rows
+
+
 def visible_pairs(Nq, L, causal):
     """(query, key) pairs a row block attends to with L keys, causal mask aligned to the end."""
     if not causal:
@@ -293,6 +339,7 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also print one line per workload")
     ap.add_argument("--extras", action="store_true",
                     help="also print one line per key-length / bias variant")
+    ap.add_argument("--bwd", action="store_true", help="also print one line per backward workload")
     ap.add_argument("--only", default=None, help="run only this workload (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -327,7 +374,13 @@ def main():
 
     W = I.WORKLOADS
     if args.only:
-        w = W[args.only]
+        name, _, kind = args.only.partition(":")
+        w = W[name]
+        if kind == "bwd":
+            part = Backward(w, torch, fab, I)
+            wall, (ms,) = time_steps(torch, [part], args.steps, args.warmup)
+            print(json.dumps({"workload": args.only, "mean_ms": round(ms, 5), "steps": args.steps}))
+            return
         if w.n_splits:
             part = Decode(w, torch, fab, I, decode_kv_sets(torch, I, w, KV_SETS))
         else:
@@ -381,6 +434,9 @@ def main():
 
     if args.extras:
         extras(torch, fab, I, W, args.steps, args.warmup, kv)
+
+    if args.bwd:
+        backward(torch, fab, I, W, args.steps, args.warmup)
 
     if args.sweep:
         for name, wk in W.items():

@@ -194,6 +194,35 @@ SDPA_FA2_API int attn_forward(const void* q, const void* k, const void* v, void*
                  int B, int Hq, int Hkv, int Nq, int Nk, int d,
                  float scale, int causal, void* stream);
 
+/*
+ * attn_bwd_workspace_bytes -- bytes of device workspace attn_bwd needs: B*Hq*Nq*4 (one float
+ * per query row).  Returns 0 for invalid (negative) arguments.
+ */
+SDPA_FA2_API size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
+
+/*
+ * attn_bwd -- gradients of the attention forward (attn_fwd), bfloat16 in and out, fp32
+ * accumulation.  Head dimension 128 only.  Not on the pages (they only report the backward's
+ * speed): the gradients of L = sum(dout * out) by the chain rule through the forward's steps,
+ *   D_i = sum_d dout_id out_id,  P = exp(scale * q.k - lse) (masked positions 0),
+ *   dv = P^T dout,  dS = P * (dout v^T - D),  dq = scale * dS k,  dk = scale * dS^T q,
+ * with dk, dv summed over the Hq/Hkv query heads that share a K/V head.
+ *
+ *   q, dq [B, Hq, Nq, d]; k, v, dk, dv [B, Hkv, Nk, d]  bf16 (dq, dk, dv written)
+ *   out, dout [B, Hq, Nq, d] bf16: the forward output and the gradient of the loss w.r.t. it
+ *   lse [B, Hq, Nq] fp32: the forward's logsumexp (required; -inf rows get zero gradients)
+ *   workspace: at least attn_bwd_workspace_bytes(B, Hq, Nq) bytes of device memory owned by the
+ *     caller (D, overwritten); calls that share it must be stream ordered.
+ * scale and causal must be those of the forward call.  Keys that no query sees get dk = dv = 0;
+ * with Nq == 0 and Nk > 0 the call writes zeros to dk and dv.  Errors as for attn_fwd (d other
+ * than 128 is ATTN_ERR_HEADDIM; Nq, like Nk, must keep one head slice below 4 GiB).
+ */
+SDPA_FA2_API int attn_bwd(const void* q, const void* k, const void* v, const void* out,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d,
+             float scale, int causal, void* stream);
+
 /* attn_status_string -- a static, NUL-terminated description of a status code. */
 SDPA_FA2_API const char* attn_status_string(int status);
 

@@ -10,12 +10,15 @@ kernels behind a small C ABI (``include/sdpa_fa2.h``):
 * ``attn_fwd_ex`` / ``attn_decode_splitkv_ex`` -- the bf16 paths with per-batch key lengths
   (``seqlens_k``) and an additive bias;
 * ``attn_forward`` -- one entry for any query length: split-KV below 32 query rows, prefill
-  otherwise.
+  otherwise;
+* ``attn_bwd`` -- the gradients dq, dk, dv of the forward (head dim 128).
 
 The Python functions here only marshal torch tensors into the C ABI (``binding.py``).
 """
 from .binding import (  # noqa: F401
     AttentionError,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
     attn_decode_num_splits,
     attn_decode_splitkv,
     attn_decode_splitkv_ex,

@@ -33,6 +33,8 @@ _SIGNATURES = {
     "attn_forward_workspace_bytes": (_c_size, [_c_int] * 6),
     "attn_forward": (_c_int, [_vp] * 6 + [_c_size] + [_vp, _vp, _c_int, _c_int] + [_c_int] * 6 +
                      [_c_float, _c_int, _vp]),
+    "attn_bwd_workspace_bytes": (_c_size, [_c_int] * 3),
+    "attn_bwd": (_c_int, [_vp] * 10 + [_c_size] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_c_int]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -277,6 +279,56 @@ def attn_forward(q, k, v, causal: bool = True, scale: float = 0.0, seqlens_k=Non
                              int(bool(causal)), _stream(q.device))
     _check_rc(rc, "attn_forward")
     return out, lse, workspace
+
+
+def attn_bwd(q, k, v, out, lse, dout, causal: bool = True, scale: float = 0.0, dq=None, dk=None,
+             dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of the forward on bf16 [B,H,N,128] tensors, given the forward's
+    output and logsumexp and the gradient ``dout`` of the loss w.r.t. the output."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    for name, t, dt in (("out", out, torch.bfloat16), ("dout", dout, torch.bfloat16)):
+        if not isinstance(t, torch.Tensor) or t.dtype != dt or t.shape != q.shape or \
+                not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous {dt} tensor shaped like q")
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or
+            tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be the forward's contiguous float32 [B, Hq, Nq] logsumexp")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                         _ptr(dk), _ptr(dv), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
+                         float(scale), int(bool(causal)), _stream(q.device))
+    _check_rc(rc, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_workspace_bytes(B: int, Hq: int, Nq: int) -> int:
+    return int(load().attn_bwd_workspace_bytes(B, Hq, Nq))
+
+
+def prepare_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, causal: bool = True,
+                scale: float = 0.0):
+    """A zero-argument callable that enqueues ``attn_bwd`` with these tensors (timing loops)."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    fn = load().attn_bwd
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq, Hkv,
+            Nq, Nk, d, float(scale), int(bool(causal)), _stream(q.device))
+
+    def call():
+        rc = fn(*args)
+        if rc != ATTN_OK:
+            _check_rc(rc, "attn_bwd")
+    return call
 
 
 def prepare_fwd(q, k, v, out, lse=None, causal: bool = True, scale: float = 0.0, seqlens_k=None,

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libsdpa_fa2.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "api.cpp"]
+SOURCES = ["fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip", "api.cpp"]
 ARCH = "gfx950"
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",

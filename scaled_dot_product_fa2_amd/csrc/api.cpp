@@ -201,6 +201,57 @@ int attn_forward(const void* q, const void* k, const void* v, void* out, float* 
                                 attn_decode_num_splits(B, Hq, Hkv, Nq, Nk), stream);
 }
 
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
+  if (B < 0 || Hq < 0 || Nq < 0) return 0;
+  uint64_t x = (uint64_t)B;
+  if (!mul_ok(x, (uint64_t)Hq, &x) || !mul_ok(x, (uint64_t)Nq, &x) || !mul_ok(x, 4u, &x) ||
+      x > (uint64_t)SIZE_MAX)
+    return 0;
+  return (size_t)x;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             int causal, void* stream) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d < 0) return ATTN_ERR_SHAPE;
+  if (Nq >= kMaxSeq || Nk >= kMaxSeq) return ATTN_ERR_SHAPE;
+  uint64_t tmp;
+  if (!numel4(B, Hq, Nq, d, &tmp) || !numel4(B, Hkv, Nk, d, &tmp)) return ATTN_ERR_SHAPE;
+  if (d != 128) return ATTN_ERR_HEADDIM;
+  if (((uint64_t)Nk + 128u) * (uint64_t)d * 2u > 0xffffffffull ||
+      ((uint64_t)Nq + 128u) * (uint64_t)d * 2u > 0xffffffffull)
+    return ATTN_ERR_SHAPE;
+  if ((Hq > 0 || Hkv > 0) && (Hkv < 1 || Hq % Hkv != 0)) return ATTN_ERR_GQA;
+  if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  const bool has_q = (uint64_t)B * (uint64_t)Hq * (uint64_t)Nq > 0;
+  const bool has_k = (uint64_t)B * (uint64_t)Hkv * (uint64_t)Nk > 0;
+  if (!has_q && !has_k) return ATTN_OK;
+  if (has_q && (q == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
+                dq == nullptr))
+    return ATTN_ERR_NULL;
+  if (has_k && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return ATTN_ERR_NULL;
+  if (has_q && (!aligned(q, 16) || !aligned(out, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+                !aligned(lse, 4)))
+    return ATTN_ERR_ALIGN;
+  if (has_k && (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16)))
+    return ATTN_ERR_ALIGN;
+  if (has_q) {
+    const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
+    if (need == 0 || workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+  }
+  const long long gq = (long long)B * Hq * ((Nq + 127) / 128);
+  const long long gk = (long long)B * Hkv * ((Nk + 127) / 128);
+  if (gq > 0x7fffffffLL || gk > 0x7fffffffLL || (long long)B * Hq * Nq / 16 > 0x7fffffffLL)
+    return ATTN_ERR_SHAPE;
+  const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
+  return launch_status(fa::launch_bwd_bf16(q, k, v, out, lse, dout, dq, dk, dv, (float*)workspace,
+                                           s, resolve_scale(scale, d), causal != 0,
+                                           (hipStream_t)stream));
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

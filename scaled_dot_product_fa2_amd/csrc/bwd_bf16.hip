@@ -1,0 +1,407 @@
+// Attention backward for gfx950, bf16 in/out, fp32 accumulation (head dim 128).
+//
+// Not on the pages (they give only the speedups of the backward pass).  The gradients of
+// L = sum(dO * O) through O = softmax(scale * Q K^T + causal mask) V are, with P recomputed from
+// the forward's logsumexp (P = exp(scale * S - LSE)):
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D_i = sum_d dO_id O_id,
+//     dQ = scale * dS K,   dK = scale * dS^T Q,
+// (D_i equals sum_k P_ik dP_ik, the softmax Jacobian's centring term, because O = P V).  Key and
+// value heads shared by several query heads receive the sum over those heads.
+//
+// gfx950 mapping, three launches on one stream:
+//   * bwd_prep_kernel: D for every query row (16 lanes per row).
+//   * bwd_dq_kernel: the forward's structure.  A workgroup owns 128 query rows (32 per wave, Q
+//     and dO held in registers as the B operand); 64-key blocks of K and V stream HBM -> LDS.
+//     S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 put one query per lane, so P and
+//     dS are per-lane formulas with the row's LSE and D; dQ^T += K^T dS^T takes K^T from the
+//     transposing LDS read and dS^T straight from the registers.
+//   * bwd_dkdv_kernel: the transpose of that.  A workgroup owns 128 keys (32 per wave, K and V
+//     in registers); 64-row blocks of Q and dO (and their LSE, D) stream through LDS, over every
+//     query head that shares the K/V head.  S = Q K^T and dP = dO V^T put one key per lane;
+//     dV^T += dO^T P and dK^T += Q^T dS, so dK and dV need no atomics and are deterministic.
+//   The LDS tiles use one XOR swizzle, chunk c of row r at c ^ ((r & 3) << 2 | (r >> 2) & 3),
+//   under which both access patterns are conflict-free: 16 consecutive rows at one chunk (the
+//   row-wise operand reads) and 4 consecutive rows x 4 chunks (the transposing reads).
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+#include <math.h>
+
+namespace fa {
+namespace {
+
+constexpr int BD = 128;            // head dim
+constexpr int BT = 64;             // rows per streamed block (keys in dq, queries in dkdv)
+constexpr int TILE = BT * BD;      // bf16 elements of one block
+constexpr int NCB = BD / 16;       // 16-dim slices per product
+
+__device__ __forceinline__ int jswz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// The lane's byte offsets inside a swizzled [rows][128] tile.
+//   row_base: row-wise A operand (rows x dims): lane (l32, h) reads row l32, dims 16c + 8h .. +7;
+//     the address of slice c is row_base ^ (32 c); rows 32..63 are + 32 * 256 bytes.
+//   tr_base: transposing A operand (dims x rows) for the key/query order of the C layout; the
+//     operand of dim block db over rows R + (0..7, 8..15) is read at
+//     ((tr_base ^ (64 db)) + R * 256) and ((tr_base ^ (64 db) ^ 32) + (R + 8) * 256), R = 16 g.
+struct TileLanes {
+  uint32_t row_base, tr_base;
+};
+__device__ __forceinline__ TileLanes tile_lanes(int lane) {
+  const int h = lane >> 5, l32 = lane & 31;
+  const int tr_g = lane >> 4, tr_j = (lane & 15) >> 2, tr_t = lane & 3;
+  const int r0 = 4 * h + tr_j, cl = 2 * (tr_g & 1) + (tr_t >> 1);
+  TileLanes t;
+  t.row_base = (uint32_t)(l32 * 256 + 16 * (h ^ jswz(l32)));
+  t.tr_base = (uint32_t)(r0 * 256 + 16 * (cl ^ jswz(r0)) + 8 * (tr_t & 1));
+  return t;
+}
+__device__ __forceinline__ u32x4 read_row(const uint16_t* tile, uint32_t row_base, int half, int c) {
+  return *(const u32x4*)((const char*)tile + half * 32 * 256 + (row_base ^ (32u * c)));
+}
+__device__ __forceinline__ bf16x8 read_tr(const uint16_t* tile, uint32_t tr_base, int R, int db) {
+  const char* b = (const char*)tile;
+  const uint32_t a = tr_base ^ (64u * db);
+  return lds_read_tr16_pair((const uint16_t*)(b + a + R * 256),
+                            (const uint16_t*)(b + (a ^ 32u) + (R + 8) * 256));
+}
+
+// Copy rows [r0, r0 + 64) of a [n_rows][128] bf16 matrix into a swizzled LDS tile: 4 waves x
+// 4 loads of 1 KB (four rows each); rows at or past n_rows read as zero.  Load i of wave w fills
+// rows 4 (4 i + w) .. +3, so the swizzled chunk of a lane does not depend on i.
+__device__ __forceinline__ void copy_tile(const uint16_t* g, int r0, int n_rows, uint16_t* dst,
+                                          int wave, int lane) {
+  const uint32_t skip = (uint32_t)min(r0, n_rows) * (BD * 2);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g + (size_t)skip / 2, (uint32_t)n_rows * BD * 2 - skip);
+  const int ld_row = lane >> 4, ld_chunk = lane & 15;
+  const int row = wave * 4 + ld_row;
+  const uint32_t voff = (uint32_t)row * 256 + 16u * (ld_chunk ^ jswz(row));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_lds_16(rs, dst + (4 * i + wave) * 512, voff, (uint32_t)i * 4096);
+}
+
+// bf16 stores of one lane's C-layout accumulators (dims x rows, lane = row): 32 dims per tile
+__device__ __forceinline__ void store_rowT(uint16_t* row_ptr, const f32x16 (&acc)[4], float mul,
+                                           int h) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const u32x2 w = {pack_bf16x2(acc[db][4 * g4 + 0] * mul, acc[db][4 * g4 + 1] * mul),
+                       pack_bf16x2(acc[db][4 * g4 + 2] * mul, acc[db][4 * g4 + 3] * mul)};
+      *(u32x2*)(row_ptr + 32 * db + 8 * g4 + 4 * h) = w;
+    }
+}
+
+// D[row] = sum_d dO[row][d] * O[row][d]; 16 lanes per row, 8 dims each.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O,
+                                                       const uint16_t* __restrict__ dO,
+                                                       float* __restrict__ Dd, long long rows) {
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = *(const u32x4*)(O + row * BD + 8 * sub);
+    const u32x4 g = *(const u32x4*)(dO + row * BD + 8 * sub);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc += __uint_as_float(o[i] << 16) * __uint_as_float(g[i] << 16);
+      acc += __uint_as_float(o[i] & 0xffff0000u) * __uint_as_float(g[i] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int m = 8; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && sub == 0) Dd[row] = acc;
+}
+
+// The per-lane P and dS of one C tile from its scores s and dP values (both in place: s -> P,
+// dp -> dS), given the reference (LSE in log2 units) and D of each element.
+__device__ __forceinline__ void p_and_ds(float& s, float& dp, float c, float lse2, float dd) {
+  const float p = fast_exp2(fmaf(s, c, -lse2));
+  s = p;
+  dp = p * (dp - dd);
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ: workgroup = 4 waves = 128 query rows; 64-key blocks of K and V through LDS.
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dd, uint16_t* __restrict__ dQ,
+    int Hq, int Hkv, int Nq, int Nk, int nqt, float scale, float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) uint16_t kl0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kl1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vl0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t vl1[TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int BH = gridDim.x / nqt;
+  const int bh = blockIdx.x % BH, qt = nqt - 1 - blockIdx.x / BH;  // heaviest blocks first
+  const int b = bh / Hq, hq = bh - b * Hq, hkv = hq / (Hq / Hkv);
+  const int off = Nk - Nq;
+  const int qw0 = qt * 128 + wave * 32, my_q = qw0 + l32;
+  const uint16_t* kg = K + (size_t)(b * Hkv + hkv) * Nk * BD;
+  const uint16_t* vg = V + (size_t)(b * Hkv + hkv) * Nk * BD;
+
+  int kv_end = Nk;
+  if (CAUSAL) kv_end = min(Nk, min(Nq - 1, qt * 128 + 127) + off + 1);
+  const int n_blk = kv_end > 0 ? (kv_end + BT - 1) / BT : 0;
+
+  // Q and dO of this lane's query as the B operand (dims 16c + 8h .. +7)
+  u32x4 qf[NCB], gf[NCB];
+  {
+    const bool ok = my_q < Nq;
+    const uint16_t* qrow = Q + ((size_t)bh * Nq + min(my_q, Nq - 1)) * BD;
+    const uint16_t* grow = dO + ((size_t)bh * Nq + min(my_q, Nq - 1)) * BD;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      qf[c] = ok ? *(const u32x4*)(qrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+      gf[c] = ok ? *(const u32x4*)(grow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // the row's reference in log2 units (+inf: no visible key, so every P is 0) and D
+  float lse2 = INFINITY, dd = 0.f;
+  if (my_q < Nq) {
+    const float l = LSE[(size_t)bh * Nq + my_q];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    dd = Dd[(size_t)bh * Nq + my_q];
+  }
+
+  const TileLanes tl = tile_lanes(lane);
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+
+  if (n_blk > 0) {
+    copy_tile(kg, 0, Nk, kl0, wave, lane);
+    copy_tile(vg, 0, Nk, vl0, wave, lane);
+  }
+  for (int t = 0; t < n_blk; ++t) {
+    const uint16_t* kc = (t & 1) ? kl1 : kl0;
+    const uint16_t* vc = (t & 1) ? vl1 : vl0;
+    wait_vmem();
+    __syncthreads();  // block t is in LDS; the other buffers are free
+    if (t + 1 < n_blk) {
+      copy_tile(kg, (t + 1) * BT, Nk, (t & 1) ? kl0 : kl1, wave, lane);
+      copy_tile(vg, (t + 1) * BT, Nk, (t & 1) ? vl0 : vl1, wave, lane);
+    }
+    if (qw0 >= Nq || (CAUSAL && t * BT > qw0 + 31 + off)) continue;
+    // S^T = K Q^T and dP^T = V dO^T: keys 32 kb + 8 (r >> 2) + 4 h + (r & 3) of this query
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        s[kb] = mfma32x32x16(read_row(kc, tl.row_base, kb, c), qf[c], s[kb]);
+        dp[kb] = mfma32x32x16(read_row(vc, tl.row_base, kb, c), gf[c], dp[kb]);
+      }
+    }
+    const int k0 = t * BT;
+    const bool need = (k0 + BT > Nk) || (CAUSAL && (k0 + BT - 1 > qw0 + off));
+    const int lim = CAUSAL ? min(Nk - 1, my_q + off) : Nk - 1;
+    u32x4 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float s0 = s[kb][r], s1 = s[kb][r + 1], d0 = dp[kb][r], d1 = dp[kb][r + 1];
+        p_and_ds(s0, d0, scale_log2, lse2, dd);
+        p_and_ds(s1, d1, scale_log2, lse2, dd);
+        if (need) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key > lim) d0 = 0.f;
+          if (key + 1 > lim) d1 = 0.f;
+        }
+        const int j = 16 * kb + r;
+        pb[j >> 3][(j >> 1) & 3] = pack_bf16x2(d0, d1);
+      }
+    // dQ^T += K^T dS^T, 16 keys at a time
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] = mfma32x32x16(read_tr(kc, tl.tr_base, 16 * g, db), pb[g], acc[db]);
+  }
+  if (my_q < Nq) store_rowT(dQ + ((size_t)bh * Nq + my_q) * BD, acc, scale, h);
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK, dV: workgroup = 4 waves = 128 keys; 64-row blocks of Q, dO, LSE, D through LDS, for every
+// query head of the K/V head's group.
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dd, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, int nkt, float scale,
+    float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ql0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t ql1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t gl0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t gl1[TILE];
+  __shared__ __attribute__((aligned(16))) float sl0[2 * BT];  // LSE (log2 units), then D
+  __shared__ __attribute__((aligned(16))) float sl1[2 * BT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int BHk = gridDim.x / nkt;
+  const int bhk = blockIdx.x % BHk, kt = blockIdx.x / BHk;
+  const int b = bhk / Hkv, hkv = bhk - b * Hkv, G = Hq / Hkv;
+  const int off = Nk - Nq;
+  const int kw0 = kt * 128 + wave * 32, my_k = kw0 + l32;
+
+  // K and V of this lane's key as the B operand
+  u32x4 kf[NCB], vf[NCB];
+  {
+    const bool ok = my_k < Nk;
+    const uint16_t* krow = K + ((size_t)bhk * Nk + min(my_k, Nk - 1)) * BD;
+    const uint16_t* vrow = V + ((size_t)bhk * Nk + min(my_k, Nk - 1)) * BD;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      kf[c] = ok ? *(const u32x4*)(krow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+      vf[c] = ok ? *(const u32x4*)(vrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // query blocks that see any key of this workgroup: rows q with q + off >= kt * 128
+  const int q_first = CAUSAL ? max(0, kt * 128 - off) : 0;
+  const int qb0 = q_first / BT, nqb = (Nq + BT - 1) / BT;
+  const int per_head = max(0, nqb - qb0);
+  const int n_steps = G * per_head;
+
+  auto stage = [&](int step, uint16_t* qd, uint16_t* gd, float* sd) {
+    const int g = step / per_head, qb = qb0 + step - g * per_head;
+    const size_t bh = (size_t)b * Hq + hkv * G + g;
+    copy_tile(Q + bh * Nq * BD, qb * BT, Nq, qd, wave, lane);
+    copy_tile(dO + bh * Nq * BD, qb * BT, Nq, gd, wave, lane);
+    if (wave == 0) {  // 64 LSE then 64 D, four bytes per lane; rows past Nq read zero
+      const int q = qb * BT;
+      const uint32_t n = (uint32_t)max(0, Nq - q) * 4;
+      load_lds_4(make_rsrc(LSE + bh * Nq + min(q, Nq), n), sd, (uint32_t)lane * 4);
+      load_lds_4(make_rsrc(Dd + bh * Nq + min(q, Nq), n), sd + BT, (uint32_t)lane * 4);
+    }
+  };
+
+  const TileLanes tl = tile_lanes(lane);
+  f32x16 ak[4], av[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ak[i] = f32x16{};
+    av[i] = f32x16{};
+  }
+
+  if (n_steps > 0) stage(0, ql0, gl0, sl0);
+  for (int t = 0; t < n_steps; ++t) {
+    const uint16_t* qc = (t & 1) ? ql1 : ql0;
+    const uint16_t* gc = (t & 1) ? gl1 : gl0;
+    const float* sc = (t & 1) ? sl1 : sl0;
+    wait_vmem();
+    __syncthreads();  // step t's blocks are in LDS; the other buffers are free
+    if (t + 1 < n_steps) stage(t + 1, (t & 1) ? ql0 : ql1, (t & 1) ? gl0 : gl1, (t & 1) ? sl0 : sl1);
+    const int qb = qb0 + t % per_head;
+    const int q0 = qb * BT;
+    if (kw0 >= Nk || (CAUSAL && q0 + BT - 1 + off < kw0)) continue;  // nothing visible
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int qh0 = q0 + 32 * half;
+      if (CAUSAL && qh0 + 31 + off < kw0) continue;
+      // S = Q K^T and dP = dO V^T: queries qh0 + 8 (r >> 2) + 4 h + (r & 3) of this key
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        s = mfma32x32x16(read_row(qc, tl.row_base, half, c), kf[c], s);
+        dp = mfma32x32x16(read_row(gc, tl.row_base, half, c), vf[c], dp);
+      }
+      const bool need = (qh0 + 32 > Nq) || (kw0 + 32 > Nk) || (CAUSAL && kw0 + 31 > qh0 + off);
+      u32x4 pp[2], pd[2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qi = 32 * half + 8 * g4 + 4 * h;  // first of this lane's four rows
+        const f32x4 l4 = *(const f32x4*)(sc + qi);
+        const f32x4 d4 = *(const f32x4*)(sc + BT + qi);
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const int r = 4 * g4 + e;
+          float s0 = s[r], s1 = s[r + 1], d0 = dp[r], d1 = dp[r + 1];
+          // LSE -inf (a row with no visible key) or a row past Nq: every P of the row is 0
+          const float la = l4[e] == -INFINITY ? INFINITY : l4[e] * kLog2e;
+          const float lb = l4[e + 1] == -INFINITY ? INFINITY : l4[e + 1] * kLog2e;
+          p_and_ds(s0, d0, scale_log2, la, d4[e]);
+          p_and_ds(s1, d1, scale_log2, lb, d4[e + 1]);
+          if (need) {
+            const int q = q0 + qi + e;
+            const bool ok0 = q < Nq && my_k < Nk && (!CAUSAL || my_k <= q + off);
+            const bool ok1 = q + 1 < Nq && my_k < Nk && (!CAUSAL || my_k <= q + 1 + off);
+            if (!ok0) s0 = d0 = 0.f;
+            if (!ok1) s1 = d1 = 0.f;
+          }
+          pp[r >> 3][(r >> 1) & 3] = pack_bf16x2(s0, s1);
+          pd[r >> 3][(r >> 1) & 3] = pack_bf16x2(d0, d1);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          av[db] = mfma32x32x16(read_tr(gc, tl.tr_base, 32 * half + 16 * g, db), pp[g], av[db]);
+          ak[db] = mfma32x32x16(read_tr(qc, tl.tr_base, 32 * half + 16 * g, db), pd[g], ak[db]);
+        }
+    }
+  }
+  if (my_k < Nk) {
+    store_rowT(dK + ((size_t)bhk * Nk + my_k) * BD, ak, scale, h);
+    store_rowT(dV + ((size_t)bhk * Nk + my_k) * BD, av, 1.f, h);
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, float* ws_d, const AttnShape& s,
+                  float scale, hipStream_t stream) {
+  const long long rows = (long long)s.B * s.Hq * s.Nq;
+  const int nqt = (s.Nq + 127) / 128, nkt = (s.Nk + 127) / 128;
+  const long long g_prep = (rows + 15) / 16;
+  const long long g_dq = (long long)s.B * s.Hq * nqt, g_kv = (long long)s.B * s.Hkv * nkt;
+  if (g_prep > 0x7fffffffLL || g_dq > 0x7fffffffLL || g_kv > 0x7fffffffLL)
+    return hipErrorInvalidConfiguration;
+  hipError_t e = hipSuccess;
+  if (g_prep > 0) {
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)g_prep), dim3(256), 0, stream,
+                       (const uint16_t*)out, (const uint16_t*)dout, ws_d, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (g_kv > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)g_kv), dim3(256), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                       (const uint16_t*)dout, lse, (const float*)ws_d, (uint16_t*)dk,
+                       (uint16_t*)dv, s.Hq, s.Hkv, s.Nq, s.Nk, nkt, scale, scale * kLog2e);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (g_dq > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL>), dim3((unsigned)g_dq), dim3(256), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                       (const uint16_t*)dout, lse, (const float*)ws_d, (uint16_t*)dq, s.Hq,
+                       s.Hkv, s.Nq, s.Nk, nqt, scale, scale * kLog2e);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* ws_d, const AttnShape& s, float scale, bool causal,
+                           hipStream_t stream) {
+  return causal ? launch<true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream)
+                : launch<false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream);
+}
+
+}  // namespace fa

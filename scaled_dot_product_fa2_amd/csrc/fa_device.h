@@ -103,6 +103,13 @@ __device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t rsrc, void* l
       rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, (int)soff, 0, 0);
 }
 
+// The same with 4 bytes per lane: lane i's bytes land at `lds_base` + 4 i.
+__device__ __forceinline__ void load_lds_4(__amdgpu_buffer_rsrc_t rsrc, void* lds_base,
+                                           uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)lds_base, 4, (int)voff, 0, 0, 0);
+}
+
 // 16 bytes per lane from `rsrc` at byte offset voff + soff into registers (zero past the end),
 // marked non-temporal (cache-policy bit 1): for data read exactly once, such as the keys and
 // values a decode split streams, this measured ~15% faster than the default policy on gfx950.

@@ -77,6 +77,13 @@ def draw_qkv(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
     return QKV(q=q, k=k, v=v, dtype=dtype)
 
 
+def draw_grad(seed: int, shape) -> np.ndarray:
+    """An output gradient (the dO of a backward pass): i.i.d. N(0, 1) from a seeded PCG64,
+    rounded to bfloat16 bits."""
+    rng = np.random.default_rng(seed)
+    return bf16_bits_from_f32(rng.standard_normal(tuple(shape), dtype=np.float32))
+
+
 def draw_seqlens(seed: int, B: int, Nk: int, edges: bool = True) -> np.ndarray:
     """Per-batch key lengths, int32 [B]: uniform in [1, Nk] from a seeded PCG64.  With ``edges``
     the first entries become Nk, 0 and 1 (all keys, none, a single key), as far as B allows."""

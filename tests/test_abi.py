@@ -222,3 +222,32 @@ def test_forward_workspace_and_routing(lib):
     assert fwd(ws_bytes=1, Nq=31, Nk=64) == C["ATTN_ERR_WORKSPACE"]
     assert fwd(ws=None, Nq=8, d=96) == C["ATTN_ERR_HEADDIM"]
     assert fwd(ws=None, B=0) == C["ATTN_OK"]
+
+
+def _bwd(lib, ws=A16, ws_bytes=1 << 40, lse=A16, dout=A16, dq=A16, dk=A16, dv=A16, q=A16, k=A16,
+         v=A16, o=A16, **kw):
+    a = {**GOOD, **kw}
+    return lib.attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, a["B"], a["Hq"], a["Hkv"],
+                        a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], None)
+
+
+def test_backward_validation(lib):
+    assert lib.attn_bwd_workspace_bytes(2, 16, 2048) == 2 * 16 * 2048 * 4
+    assert lib.attn_bwd_workspace_bytes(-1, 16, 2048) == 0
+    assert _bwd(lib, d=64) == C["ATTN_ERR_HEADDIM"]  # head dim 128 only
+    assert _bwd(lib, B=-1) == C["ATTN_ERR_SHAPE"]
+    assert _bwd(lib, Hq=3) == C["ATTN_ERR_GQA"]
+    assert _bwd(lib, scale=float("nan")) == C["ATTN_ERR_SCALE"]
+    for name in ("lse", "dout", "dq", "q", "o", "k", "v", "dk", "dv"):
+        assert _bwd(lib, **{name: None}) == C["ATTN_ERR_NULL"], name
+    assert _bwd(lib, dq=A16 + 8) == C["ATTN_ERR_ALIGN"]
+    assert _bwd(lib, lse=A16 + 2) == C["ATTN_ERR_ALIGN"]
+    assert _bwd(lib, ws=None) == C["ATTN_ERR_WORKSPACE"]
+    assert _bwd(lib, ws_bytes=lib.attn_bwd_workspace_bytes(1, 4, 8) - 1) == C["ATTN_ERR_WORKSPACE"]
+    assert _bwd(lib, ws=A16 + 4) == C["ATTN_ERR_ALIGN"]
+    # nothing on either side: nothing to do, NULL everywhere is fine
+    assert _bwd(lib, B=0, q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None,
+                dv=None, ws=None) == C["ATTN_OK"]
+    # no query rows: the query-side pointers and the workspace are not needed (dk, dv are)
+    assert _bwd(lib, Nq=0, q=None, o=None, lse=None, dout=None, dq=None, ws=None, k=None) == \
+        C["ATTN_ERR_NULL"]

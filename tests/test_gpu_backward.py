@@ -1,0 +1,129 @@
+"""GPU parity of the backward pass (attn_bwd) against the CPU fp64 oracle's gradients.
+
+The forward runs on the GPU first (its bf16 output and fp32 logsumexp are the backward's
+inputs, as in training); the oracle differentiates the definition from the same bf16 q, k, v and
+dout.  Every call goes through the C ABI."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from gpu_helpers import say, to_f64, upload  # noqa: E402
+from oracle import attention as A  # noqa: E402
+from scaled_dot_product_fa2_amd import binding as fa  # noqa: E402
+from scaled_dot_product_fa2_amd import inputs as I  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+# Tolerances relative to the largest reference gradient of each tensor.  The kernels round P and
+# dS to bf16 for the matrix cores (relative 2^-9 each), take D from the bf16 forward output and
+# store bf16 gradients (another 2^-9); with sums over hundreds of terms the elementwise error
+# stays a small multiple of 2^-9 of the largest entry.
+GRAD_MAX_REL = 2e-2    # max |gpu - ref| / max |ref|
+GRAD_MEAN_REL = 2e-3   # mean |gpu - ref| / max |ref|
+# A gradient that is exactly zero (one key: the softmax is constant, so dq = dk = 0) is compared
+# on an absolute scale instead: P and D carry fp32/bf16 rounding, so the GPU's value is tiny,
+# not zero.
+GRAD_FLOOR = 2.0 ** -10
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    fa.load()
+    yield
+
+
+def _s32(d):
+    return float(np.float32(1.0 / np.sqrt(d)))
+
+
+def _check(name, got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{name}: non-finite gradient"
+    scale = max(float(np.abs(ref).max(initial=0.0)), GRAD_FLOOR)
+    err = np.abs(got - ref)
+    mx, mean = float(err.max(initial=0.0)) / scale, (float(err.mean()) / scale if err.size else 0.0)
+    say(f"  {name}: max|ref|={scale:.3e} max_rel={mx:.3e} mean_rel={mean:.3e}")
+    assert mx <= GRAD_MAX_REL, f"{name}: max error {mx} of max|ref| > {GRAD_MAX_REL}"
+    assert mean <= GRAD_MEAN_REL, f"{name}: mean error {mean} of max|ref| > {GRAD_MEAN_REL}"
+
+
+def _run(B, Hq, Hkv, Nq, Nk, causal, seed, d=128):
+    x = I.draw_qkv(seed, B, Hq, Hkv, Nq, Nk, d)
+    g_bits = I.draw_grad(seed + 1, (B, Hq, Nq, d))
+    q, k, v = upload(x)
+    dout = I.to_device(g_bits, "bf16")
+    s32 = _s32(d)
+    say(f"backward B{B} Hq{Hq} Hkv{Hkv} Nq{Nq} Nk{Nk} causal={causal} seed={seed}")
+    out, lse = fa.attn_fwd(q, k, v, causal=causal, scale=s32)
+    dq, dk, dv = fa.attn_bwd(q, k, v, out, lse, dout, causal=causal, scale=s32)
+    torch.cuda.synchronize()
+    g = I.bf16_bits_to_f32(g_bits).astype(np.float64)
+    rq, rk, rv = A.attention_backward_fp64(*x.as_f64(), g, s32, causal)
+    return (to_f64(dq), to_f64(dk), to_f64(dv)), (rq, rk, rv), (q, k, v, out, lse, dout)
+
+
+# (B, Hq, Hkv, Nq, Nk, causal): one and several 64/128-row blocks with ragged tails, GQA groups of
+# 1, 2 and 4, Nq != Nk both ways (the first rows without any key), a single key, non-causal
+CASES = [
+    (1, 2, 2, 128, 128, True),
+    (2, 4, 2, 200, 200, True),
+    (1, 4, 1, 257, 257, False),
+    (1, 2, 1, 130, 300, True),
+    (1, 2, 2, 300, 130, True),
+    (2, 2, 2, 77, 1, True),
+    (1, 8, 2, 64, 512, False),
+    (2, 8, 8, 384, 384, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_Nq{}_Nk{}_{}".format(
+    *c[:5], "causal" if c[5] else "full"))
+def test_backward_matches_oracle(case):
+    B, Hq, Hkv, Nq, Nk, causal = case
+    got, ref, _ = _run(B, Hq, Hkv, Nq, Nk, causal, seed=4000 + Nq + 3 * Nk)
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        _check(name, a, r)
+
+
+def test_backward_long_causal():
+    # B=1, H=4, N=1024, causal: 16 key blocks of 64 per query block, 8 query blocks per key block
+    got, ref, _ = _run(1, 4, 4, 1024, 1024, True, seed=4100)
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        _check(name, a, r)
+
+
+def test_backward_deterministic_and_fully_written():
+    got, _, (q, k, v, out, lse, dout) = _run(2, 4, 2, 200, 333, True, seed=4200)
+    s32 = _s32(128)
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    fa.attn_bwd(q, k, v, out, lse, dout, causal=True, scale=s32, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), got):
+        assert not bool(torch.isnan(a.float()).any()), f"{name} not fully written"
+        assert np.array_equal(to_f64(a), b), f"{name} differs between two identical calls"
+
+
+def test_backward_without_query_rows_zeroes_dk_dv():
+    say("backward Nq=0")
+    k = torch.ones((1, 2, 70, 128), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    out, dout = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((1, 2, 0), dtype=torch.float32, device="cuda")
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(k, float("nan"))
+    fa.attn_bwd(q, k, k.clone(), out, lse, dout, causal=True, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert bool((dk.float() == 0).all()) and bool((dv.float() == 0).all())
+
+
+def test_backward_rejects_other_head_dims():
+    q = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 2, 8), dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.AttentionError, match="head dimension"):
+        fa.attn_bwd(q, q, q, q, lse, q)
