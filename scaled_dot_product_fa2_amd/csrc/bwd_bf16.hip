@@ -18,7 +18,9 @@
 //   * bwd_dkdv_kernel: the transpose of that.  A workgroup owns 128 keys (32 per wave, K and V
 //     in registers); 64-row blocks of Q and dO (and their LSE, D) stream through LDS, over every
 //     query head that shares the K/V head.  S = Q K^T and dP = dO V^T put one key per lane;
-//     dV^T += dO^T P and dK^T += Q^T dS, so dK and dV need no atomics and are deterministic.
+//     half of the workgroups accumulate dV^T += dO^T P, the other half dK^T += Q^T dS, so a
+//     wave holds one accumulator set and two workgroups fit a CU (S is computed by both halves).
+//     dK and dV need no atomics and are deterministic.
 //   The LDS tiles use one XOR swizzle, chunk c of row r at c ^ ((r & 3) << 2 | (r >> 2) & 3),
 //   under which both access patterns are conflict-free: 16 consecutive rows at one chunk (the
 //   row-wise operand reads) and 4 consecutive rows x 4 chunks (the transposing reads).
@@ -124,7 +126,7 @@ __device__ __forceinline__ void p_and_ds(float& s, float& dp, float c, float lse
 // ---------------------------------------------------------------------------------------------
 // dQ: workgroup = 4 waves = 128 query rows; 64-key blocks of K and V through LDS.
 template <bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dd, uint16_t* __restrict__ dQ,
@@ -188,27 +190,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       copy_tile(vg, (t + 1) * BT, Nk, (t & 1) ? vl0 : vl1, wave, lane);
     }
     if (qw0 >= Nq || (CAUSAL && t * BT > qw0 + 31 + off)) continue;
-    // S^T = K Q^T and dP^T = V dO^T: keys 32 kb + 8 (r >> 2) + 4 h + (r & 3) of this query
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        s[kb] = mfma32x32x16(read_row(kc, tl.row_base, kb, c), qf[c], s[kb]);
-        dp[kb] = mfma32x32x16(read_row(vc, tl.row_base, kb, c), gf[c], dp[kb]);
-      }
-    }
+    // S^T = K Q^T and dP^T = V dO^T, 32 keys at a time (keys 32 kb + 8 (r >> 2) + 4 h + (r & 3)
+    // of this query), each half turned into its dS^T operands before the next is computed
     const int k0 = t * BT;
     const bool need = (k0 + BT > Nk) || (CAUSAL && (k0 + BT - 1 > qw0 + off));
     const int lim = CAUSAL ? min(Nk - 1, my_q + off) : Nk - 1;
     u32x4 pb[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        s = mfma32x32x16(read_row(kc, tl.row_base, kb, c), qf[c], s);
+        dp = mfma32x32x16(read_row(vc, tl.row_base, kb, c), gf[c], dp);
+      }
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float s0 = s[kb][r], s1 = s[kb][r + 1], d0 = dp[kb][r], d1 = dp[kb][r + 1];
+        float s0 = s[r], s1 = s[r + 1], d0 = dp[r], d1 = dp[r + 1];
         p_and_ds(s0, d0, scale_log2, lse2, dd);
         p_and_ds(s1, d1, scale_log2, lse2, dd);
         if (need) {
@@ -219,6 +217,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
         const int j = 16 * kb + r;
         pb[j >> 3][(j >> 1) & 3] = pack_bf16x2(d0, d1);
       }
+    }
     // dQ^T += K^T dS^T, 16 keys at a time
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -229,10 +228,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: workgroup = 4 waves = 128 keys; 64-row blocks of Q, dO, LSE, D through LDS, for every
-// query head of the K/V head's group.
+// dK or dV: workgroup = 4 waves = 128 keys; 64-row blocks of Q, dO, LSE, D through LDS, for
+// every query head of the K/V head's group.  Even workgroups accumulate dV (from P), odd ones dK
+// (from dS): one accumulator set per wave keeps two workgroups per CU, at the price of S
+// computed by both.
 template <bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dd, uint16_t* __restrict__ dK,
@@ -248,13 +249,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int BHk = gridDim.x / nkt;
-  const int bhk = blockIdx.x % BHk, kt = blockIdx.x / BHk;
+  const bool do_k = blockIdx.x & 1;
+  const int unit = blockIdx.x >> 1;
+  const int BHk = (gridDim.x >> 1) / nkt;
+  const int bhk = unit % BHk, kt = unit / BHk;
   const int b = bhk / Hkv, hkv = bhk - b * Hkv, G = Hq / Hkv;
   const int off = Nk - Nq;
   const int kw0 = kt * 128 + wave * 32, my_k = kw0 + l32;
 
-  // K and V of this lane's key as the B operand
+  // K (and for dK, V) of this lane's key as the B operand
   u32x4 kf[NCB], vf[NCB];
   {
     const bool ok = my_k < Nk;
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
       kf[c] = ok ? *(const u32x4*)(krow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
-      vf[c] = ok ? *(const u32x4*)(vrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+      vf[c] = ok && do_k ? *(const u32x4*)(vrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -287,12 +290,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   };
 
   const TileLanes tl = tile_lanes(lane);
-  f32x16 ak[4], av[4];
+  f32x16 acc[4];  // dK^T or dV^T of this wave's keys
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ak[i] = f32x16{};
-    av[i] = f32x16{};
-  }
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 
   if (n_steps > 0) stage(0, ql0, gl0, sl0);
   for (int t = 0; t < n_steps; ++t) {
@@ -309,15 +309,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     for (int half = 0; half < 2; ++half) {
       const int qh0 = q0 + 32 * half;
       if (CAUSAL && qh0 + 31 + off < kw0) continue;
-      // S = Q K^T and dP = dO V^T: queries qh0 + 8 (r >> 2) + 4 h + (r & 3) of this key
+      // S = Q K^T (and for dK, dP = dO V^T): queries qh0 + 8 (r >> 2) + 4 h + (r & 3) of this key
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
         s = mfma32x32x16(read_row(qc, tl.row_base, half, c), kf[c], s);
-        dp = mfma32x32x16(read_row(gc, tl.row_base, half, c), vf[c], dp);
+        if (do_k) dp = mfma32x32x16(read_row(gc, tl.row_base, half, c), vf[c], dp);
       }
       const bool need = (qh0 + 32 > Nq) || (kw0 + 32 > Nk) || (CAUSAL && kw0 + 31 > qh0 + off);
-      u32x4 pp[2], pd[2];
+      u32x4 pb[2];  // P (for dV) or dS (for dK) as the B operand
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int qi = 32 * half + 8 * g4 + 4 * h;  // first of this lane's four rows
@@ -339,24 +339,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             if (!ok0) s0 = d0 = 0.f;
             if (!ok1) s1 = d1 = 0.f;
           }
-          pp[r >> 3][(r >> 1) & 3] = pack_bf16x2(s0, s1);
-          pd[r >> 3][(r >> 1) & 3] = pack_bf16x2(d0, d1);
+          pb[r >> 3][(r >> 1) & 3] = do_k ? pack_bf16x2(d0, d1) : pack_bf16x2(s0, s1);
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS, 16 queries at a time
+      // dK^T += Q^T dS or dV^T += dO^T P, 16 queries at a time
+      const uint16_t* at = do_k ? qc : gc;
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          av[db] = mfma32x32x16(read_tr(gc, tl.tr_base, 32 * half + 16 * g, db), pp[g], av[db]);
-          ak[db] = mfma32x32x16(read_tr(qc, tl.tr_base, 32 * half + 16 * g, db), pd[g], ak[db]);
-        }
+        for (int db = 0; db < 4; ++db)
+          acc[db] = mfma32x32x16(read_tr(at, tl.tr_base, 32 * half + 16 * g, db), pb[g], acc[db]);
     }
   }
-  if (my_k < Nk) {
-    store_rowT(dK + ((size_t)bhk * Nk + my_k) * BD, ak, scale, h);
-    store_rowT(dV + ((size_t)bhk * Nk + my_k) * BD, av, 1.f, h);
-  }
+  if (my_k < Nk)
+    store_rowT((do_k ? dK : dV) + ((size_t)bhk * Nk + my_k) * BD, acc, do_k ? scale : 1.f, h);
 }
 
 template <bool CAUSAL>
@@ -366,7 +362,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
   const long long rows = (long long)s.B * s.Hq * s.Nq;
   const int nqt = (s.Nq + 127) / 128, nkt = (s.Nk + 127) / 128;
   const long long g_prep = (rows + 15) / 16;
-  const long long g_dq = (long long)s.B * s.Hq * nqt, g_kv = (long long)s.B * s.Hkv * nkt;
+  const long long g_dq = (long long)s.B * s.Hq * nqt, g_kv = 2LL * s.B * s.Hkv * nkt;
   if (g_prep > 0x7fffffffLL || g_dq > 0x7fffffffLL || g_kv > 0x7fffffffLL)
     return hipErrorInvalidConfiguration;
   hipError_t e = hipSuccess;
