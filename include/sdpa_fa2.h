@@ -195,7 +195,7 @@ SDPA_FA2_API int attn_forward(const void* q, const void* k, const void* v, void*
                  float scale, int causal, void* stream);
 
 /*
- * attn_bwd_workspace_bytes -- bytes of device workspace attn_bwd needs: B*Hq*Nq*4 (one float
+ * attn_bwd_workspace_bytes -- bytes of device workspace attn_bwd needs: B*Hq*Nq*8 (two floats
  * per query row).  Returns 0 for invalid (negative) arguments.
  */
 SDPA_FA2_API size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
@@ -212,7 +212,8 @@ SDPA_FA2_API size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  *   out, dout [B, Hq, Nq, d] bf16: the forward output and the gradient of the loss w.r.t. it
  *   lse [B, Hq, Nq] fp32: the forward's logsumexp (required; -inf rows get zero gradients)
  *   workspace: at least attn_bwd_workspace_bytes(B, Hq, Nq) bytes of device memory owned by the
- *     caller (D, overwritten); calls that share it must be stream ordered.
+ *     caller: fp32 D [B, Hq, Nq], then lse * log2(e) [B, Hq, Nq] (+inf for -inf rows), both
+ *     overwritten; calls that share it must be stream ordered.
  * scale and causal must be those of the forward call.  Keys that no query sees get dk = dv = 0;
  * with Nq == 0 and Nk > 0 the call writes zeros to dk and dv.  Errors as for attn_fwd (d other
  * than 128 is ATTN_ERR_HEADDIM; Nq, like Nk, must keep one head slice below 4 GiB).

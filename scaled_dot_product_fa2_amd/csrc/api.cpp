@@ -204,7 +204,7 @@ int attn_forward(const void* q, const void* k, const void* v, void* out, float* 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
   if (B < 0 || Hq < 0 || Nq < 0) return 0;
   uint64_t x = (uint64_t)B;
-  if (!mul_ok(x, (uint64_t)Hq, &x) || !mul_ok(x, (uint64_t)Nq, &x) || !mul_ok(x, 4u, &x) ||
+  if (!mul_ok(x, (uint64_t)Hq, &x) || !mul_ok(x, (uint64_t)Nq, &x) || !mul_ok(x, 8u, &x) ||
       x > (uint64_t)SIZE_MAX)
     return 0;
   return (size_t)x;

@@ -18,9 +18,9 @@
 //   * bwd_dkdv_kernel: the transpose of that.  A workgroup owns 128 keys (32 per wave, K and V
 //     in registers); 64-row blocks of Q and dO (and their LSE, D) stream through LDS, over every
 //     query head that shares the K/V head.  S = Q K^T and dP = dO V^T put one key per lane;
-//     half of the workgroups accumulate dV^T += dO^T P, the other half dK^T += Q^T dS, so a
-//     wave holds one accumulator set and two workgroups fit a CU (S is computed by both halves).
-//     dK and dV need no atomics and are deterministic.
+//     eight waves share each block: four accumulate dV^T += dO^T P, four dK^T += Q^T dS, so a
+//     wave holds one accumulator set (two waves per SIMD) and S is computed by both.  dK and dV
+//     need no atomics and are deterministic.
 //   The LDS tiles use one XOR swizzle, chunk c of row r at c ^ ((r & 3) << 2 | (r >> 2) & 3),
 //   under which both access patterns are conflict-free: 16 consecutive rows at one chunk (the
 //   row-wise operand reads) and 4 consecutive rows x 4 chunks (the transposing reads).
@@ -94,10 +94,14 @@ __device__ __forceinline__ void store_rowT(uint16_t* row_ptr, const f32x16 (&acc
     }
 }
 
-// D[row] = sum_d dO[row][d] * O[row][d]; 16 lanes per row, 8 dims each.
+// D[row] = sum_d dO[row][d] * O[row][d] (16 lanes per row, 8 dims each), and the row's
+// reference for P in log2 units, L2[row] = LSE[row] * log2(e), +inf for a row with no visible key
+// (LSE = -inf) so that every P of it is exactly 0.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O,
                                                        const uint16_t* __restrict__ dO,
-                                                       float* __restrict__ Dd, long long rows) {
+                                                       const float* __restrict__ LSE,
+                                                       float* __restrict__ Dd,
+                                                       float* __restrict__ L2, long long rows) {
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   float acc = 0.f;
@@ -112,7 +116,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   }
 #pragma unroll
   for (int m = 8; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (row < rows && sub == 0) Dd[row] = acc;
+  if (row < rows && sub == 0) {
+    Dd[row] = acc;
+    const float l = LSE[row];
+    L2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
 }
 
 // The per-lane P and dS of one C tile from its scores s and dP values (both in place: s -> P,
@@ -129,7 +137,7 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Dd, uint16_t* __restrict__ dQ,
+    const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dQ,
     int Hq, int Hkv, int Nq, int Nk, int nqt, float scale, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) uint16_t kl0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t kl1[TILE];
@@ -166,8 +174,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   // the row's reference in log2 units (+inf: no visible key, so every P is 0) and D
   float lse2 = INFINITY, dd = 0.f;
   if (my_q < Nq) {
-    const float l = LSE[(size_t)bh * Nq + my_q];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    lse2 = L2[(size_t)bh * Nq + my_q];
     dd = Dd[(size_t)bh * Nq + my_q];
   }
 
@@ -228,34 +235,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK or dV: workgroup = 4 waves = 128 keys; 64-row blocks of Q, dO, LSE, D through LDS, for
-// every query head of the K/V head's group.  Even workgroups accumulate dV (from P), odd ones dK
-// (from dS): one accumulator set per wave keeps two workgroups per CU, at the price of S
-// computed by both.
+// dK and dV: workgroup = 8 waves for 128 keys; 64-row blocks of Q, dO and their references and D
+// go through LDS once for all of them, for every query head of the K/V head's group.  Waves 0-3
+// accumulate dV (from P), waves 4-7 dK (from dS), 32 keys each: a wave holds one accumulator set,
+// S is computed by both, and each SIMD pairs a dV wave with a heavier dK wave.
 template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Dd, uint16_t* __restrict__ dK,
+    const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, int nkt, float scale,
     float scale_log2) {
   __shared__ __attribute__((aligned(1024))) uint16_t ql0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t ql1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gl0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gl1[TILE];
-  __shared__ __attribute__((aligned(16))) float sl0[2 * BT];  // LSE (log2 units), then D
+  __shared__ __attribute__((aligned(16))) float sl0[2 * BT];  // reference (log2 units), then D
   __shared__ __attribute__((aligned(16))) float sl1[2 * BT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const bool do_k = blockIdx.x & 1;
-  const int unit = blockIdx.x >> 1;
-  const int BHk = (gridDim.x >> 1) / nkt;
-  const int bhk = unit % BHk, kt = unit / BHk;
+  const bool do_k = wave >= 4;
+  const int BHk = gridDim.x / nkt;
+  const int bhk = blockIdx.x % BHk, kt = blockIdx.x / BHk;
   const int b = bhk / Hkv, hkv = bhk - b * Hkv, G = Hq / Hkv;
   const int off = Nk - Nq;
-  const int kw0 = kt * 128 + wave * 32, my_k = kw0 + l32;
+  const int kw0 = kt * 128 + (wave & 3) * 32, my_k = kw0 + l32;
 
   // K (and for dK, V) of this lane's key as the B operand
   u32x4 kf[NCB], vf[NCB];
@@ -279,12 +285,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   auto stage = [&](int step, uint16_t* qd, uint16_t* gd, float* sd) {
     const int g = step / per_head, qb = qb0 + step - g * per_head;
     const size_t bh = (size_t)b * Hq + hkv * G + g;
-    copy_tile(Q + bh * Nq * BD, qb * BT, Nq, qd, wave, lane);
-    copy_tile(dO + bh * Nq * BD, qb * BT, Nq, gd, wave, lane);
-    if (wave == 0) {  // 64 LSE then 64 D, four bytes per lane; rows past Nq read zero
+    if (wave < 4)  // waves 0-3 copy the Q block, waves 4-7 the dO block
+      copy_tile(Q + bh * Nq * BD, qb * BT, Nq, qd, wave, lane);
+    else
+      copy_tile(dO + bh * Nq * BD, qb * BT, Nq, gd, wave - 4, lane);
+    if (wave == 0) {  // 64 references then 64 D, four bytes per lane; rows past Nq read zero
       const int q = qb * BT;
       const uint32_t n = (uint32_t)max(0, Nq - q) * 4;
-      load_lds_4(make_rsrc(LSE + bh * Nq + min(q, Nq), n), sd, (uint32_t)lane * 4);
+      load_lds_4(make_rsrc(L2 + bh * Nq + min(q, Nq), n), sd, (uint32_t)lane * 4);
       load_lds_4(make_rsrc(Dd + bh * Nq + min(q, Nq), n), sd + BT, (uint32_t)lane * 4);
     }
   };
@@ -327,11 +335,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         for (int e = 0; e < 4; e += 2) {
           const int r = 4 * g4 + e;
           float s0 = s[r], s1 = s[r + 1], d0 = dp[r], d1 = dp[r + 1];
-          // LSE -inf (a row with no visible key) or a row past Nq: every P of the row is 0
-          const float la = l4[e] == -INFINITY ? INFINITY : l4[e] * kLog2e;
-          const float lb = l4[e + 1] == -INFINITY ? INFINITY : l4[e + 1] * kLog2e;
-          p_and_ds(s0, d0, scale_log2, la, d4[e]);
-          p_and_ds(s1, d1, scale_log2, lb, d4[e + 1]);
+          // (rows past Nq read a reference of 0 and are masked below)
+          p_and_ds(s0, d0, scale_log2, l4[e], d4[e]);
+          p_and_ds(s1, d1, scale_log2, l4[e + 1], d4[e + 1]);
           if (need) {
             const int q = q0 + qi + e;
             const bool ok0 = q < Nq && my_k < Nk && (!CAUSAL || my_k <= q + off);
@@ -360,22 +366,23 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
                   const void* dout, void* dq, void* dk, void* dv, float* ws_d, const AttnShape& s,
                   float scale, hipStream_t stream) {
   const long long rows = (long long)s.B * s.Hq * s.Nq;
+  float* const ws_l2 = ws_d + rows;  // the workspace holds D, then the log2-unit references
   const int nqt = (s.Nq + 127) / 128, nkt = (s.Nk + 127) / 128;
   const long long g_prep = (rows + 15) / 16;
-  const long long g_dq = (long long)s.B * s.Hq * nqt, g_kv = 2LL * s.B * s.Hkv * nkt;
+  const long long g_dq = (long long)s.B * s.Hq * nqt, g_kv = (long long)s.B * s.Hkv * nkt;
   if (g_prep > 0x7fffffffLL || g_dq > 0x7fffffffLL || g_kv > 0x7fffffffLL)
     return hipErrorInvalidConfiguration;
   hipError_t e = hipSuccess;
   if (g_prep > 0) {
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)g_prep), dim3(256), 0, stream,
-                       (const uint16_t*)out, (const uint16_t*)dout, ws_d, rows);
+                       (const uint16_t*)out, (const uint16_t*)dout, lse, ws_d, ws_l2, rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (g_kv > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)g_kv), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)g_kv), dim3(512), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dout, lse, (const float*)ws_d, (uint16_t*)dk,
+                       (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dk,
                        (uint16_t*)dv, s.Hq, s.Hkv, s.Nq, s.Nk, nkt, scale, scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -383,7 +390,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
   if (g_dq > 0) {
     hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL>), dim3((unsigned)g_dq), dim3(256), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dout, lse, (const float*)ws_d, (uint16_t*)dq, s.Hq,
+                       (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dq, s.Hq,
                        s.Hkv, s.Nq, s.Nk, nqt, scale, scale * kLog2e);
     e = hipGetLastError();
   }
