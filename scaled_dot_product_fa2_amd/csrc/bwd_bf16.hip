@@ -313,19 +313,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const int qb = qb0 + t % per_head;
     const int q0 = qb * BT;
     if (kw0 >= Nk || (CAUSAL && q0 + BT - 1 + off < kw0)) continue;  // nothing visible
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    // S = Q K^T (and for dK, dP = dO V^T), 32 query rows at a time: half j holds queries
+    // q0 + 32 j + 8 (r >> 2) + 4 h + (r & 3) of this key.  The dV waves (no dP) compute both
+    // halves' independent products interleaved; the dK waves, short of registers, one half at a
+    // time with S and dP interleaved.
+    u32x4 pb[4];  // P (for dV) or dS (for dK) as the B operand, 16 queries each
+    auto finish_half = [&](int half, const f32x16& sh, const f32x16& dph) {
       const int qh0 = q0 + 32 * half;
-      if (CAUSAL && qh0 + 31 + off < kw0) continue;
-      // S = Q K^T (and for dK, dP = dO V^T): queries qh0 + 8 (r >> 2) + 4 h + (r & 3) of this key
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        s = mfma32x32x16(read_row(qc, tl.row_base, half, c), kf[c], s);
-        if (do_k) dp = mfma32x32x16(read_row(gc, tl.row_base, half, c), vf[c], dp);
-      }
       const bool need = (qh0 + 32 > Nq) || (kw0 + 32 > Nk) || (CAUSAL && kw0 + 31 > qh0 + off);
-      u32x4 pb[2];  // P (for dV) or dS (for dK) as the B operand
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int qi = 32 * half + 8 * g4 + 4 * h;  // first of this lane's four rows
@@ -334,7 +329,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
           const int r = 4 * g4 + e;
-          float s0 = s[r], s1 = s[r + 1], d0 = dp[r], d1 = dp[r + 1];
+          float s0 = sh[r], s1 = sh[r + 1], d0 = dph[r], d1 = dph[r + 1];
           // (rows past Nq read a reference of 0 and are masked below)
           p_and_ds(s0, d0, scale_log2, l4[e], d4[e]);
           p_and_ds(s1, d1, scale_log2, l4[e + 1], d4[e + 1]);
@@ -345,17 +340,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
             if (!ok0) s0 = d0 = 0.f;
             if (!ok1) s1 = d1 = 0.f;
           }
-          pb[r >> 3][(r >> 1) & 3] = do_k ? pack_bf16x2(d0, d1) : pack_bf16x2(s0, s1);
+          const int j = 16 * half + r;
+          pb[j >> 3][(j >> 1) & 3] = do_k ? pack_bf16x2(d0, d1) : pack_bf16x2(s0, s1);
         }
       }
-      // dK^T += Q^T dS or dV^T += dO^T P, 16 queries at a time
-      const uint16_t* at = do_k ? qc : gc;
+    };
+    if (do_k) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int half = 0; half < 2; ++half) {
+        f32x16 sh = f32x16{}, dph = f32x16{};
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db] = mfma32x32x16(read_tr(at, tl.tr_base, 32 * half + 16 * g, db), pb[g], acc[db]);
+        for (int c = 0; c < NCB; ++c) {
+          sh = mfma32x32x16(read_row(qc, tl.row_base, half, c), kf[c], sh);
+          dph = mfma32x32x16(read_row(gc, tl.row_base, half, c), vf[c], dph);
+        }
+        finish_half(half, sh, dph);
+      }
+    } else {
+      f32x16 s2[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          s2[half] = mfma32x32x16(read_row(qc, tl.row_base, half, c), kf[c], s2[half]);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) finish_half(half, s2[half], f32x16{});
     }
+    // dK^T += Q^T dS or dV^T += dO^T P, 16 queries at a time
+    const uint16_t* at = do_k ? qc : gc;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        acc[db] = mfma32x32x16(read_tr(at, tl.tr_base, 16 * g, db), pb[g], acc[db]);
   }
   if (my_k < Nk)
     store_rowT((do_k ? dK : dV) + ((size_t)bhk * Nk + my_k) * BD, acc, do_k ? scale : 1.f, h);
