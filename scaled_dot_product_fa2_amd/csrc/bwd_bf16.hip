@@ -313,10 +313,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const int qb = qb0 + t % per_head;
     const int q0 = qb * BT;
     if (kw0 >= Nk || (CAUSAL && q0 + BT - 1 + off < kw0)) continue;  // nothing visible
-    // S = Q K^T (and for dK, dP = dO V^T), 32 query rows at a time: half j holds queries
-    // q0 + 32 j + 8 (r >> 2) + 4 h + (r & 3) of this key.  The dV waves (no dP) compute both
-    // halves' independent products interleaved; the dK waves, short of registers, one half at a
-    // time with S and dP interleaved.
+    // S = Q K^T (and for dK, dP = dO V^T) for both 32-row halves, the independent products
+    // interleaved: half j holds queries q0 + 32 j + 8 (r >> 2) + 4 h + (r & 3) of this key.
     u32x4 pb[4];  // P (for dV) or dS (for dK) as the B operand, 16 queries each
     auto finish_half = [&](int half, const f32x16& sh, const f32x16& dph) {
       const int qh0 = q0 + 32 * half;
@@ -346,16 +344,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       }
     };
     if (do_k) {
+      f32x16 s2[2] = {f32x16{}, f32x16{}}, d2[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        f32x16 sh = f32x16{}, dph = f32x16{};
+      for (int c = 0; c < NCB; ++c)
 #pragma unroll
-        for (int c = 0; c < NCB; ++c) {
-          sh = mfma32x32x16(read_row(qc, tl.row_base, half, c), kf[c], sh);
-          dph = mfma32x32x16(read_row(gc, tl.row_base, half, c), vf[c], dph);
+        for (int half = 0; half < 2; ++half) {
+          s2[half] = mfma32x32x16(read_row(qc, tl.row_base, half, c), kf[c], s2[half]);
+          d2[half] = mfma32x32x16(read_row(gc, tl.row_base, half, c), vf[c], d2[half]);
         }
-        finish_half(half, sh, dph);
-      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) finish_half(half, s2[half], d2[half]);
     } else {
       f32x16 s2[2] = {f32x16{}, f32x16{}};
 #pragma unroll
