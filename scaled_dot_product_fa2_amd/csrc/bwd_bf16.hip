@@ -15,12 +15,12 @@
 //     S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 put one query per lane, so P and
 //     dS are per-lane formulas with the row's LSE and D; dQ^T += K^T dS^T takes K^T from the
 //     transposing LDS read and dS^T straight from the registers.
-//   * bwd_dkdv_kernel: the transpose of that.  A workgroup owns 128 keys (32 per wave, K and V
-//     in registers); 64-row blocks of Q and dO (and their LSE, D) stream through LDS, over every
-//     query head that shares the K/V head.  S = Q K^T and dP = dO V^T put one key per lane;
-//     eight waves share each block: four accumulate dV^T += dO^T P, four dK^T += Q^T dS, so a
-//     wave holds one accumulator set (two waves per SIMD) and S is computed by both.  dK and dV
-//     need no atomics and are deterministic.
+//   * bwd_dkdv_kernel: the transpose of that.  A workgroup owns 128 keys (32 per wave pair);
+//     64-row blocks of Q and dO (and their LSE, D) stream through LDS, over every query head that
+//     shares the K/V head.  S = Q K^T and dP = dO V^T put one key per lane; eight waves share each
+//     block: four compute S, P and dV^T += dO^T P, four dP and, with P passed through LDS one step
+//     later, dS and dK^T += Q^T dS, so each wave runs two products and holds one accumulator set
+//     (two waves per SIMD).  dK and dV need no atomics and are deterministic.
 //   The LDS tiles use one XOR swizzle, chunk c of row r at c ^ ((r & 3) << 2 | (r >> 2) & 3),
 //   under which both access patterns are conflict-free: 16 consecutive rows at one chunk (the
 //   row-wise operand reads) and 4 consecutive rows x 4 chunks (the transposing reads).
@@ -236,9 +236,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 // ---------------------------------------------------------------------------------------------
 // dK and dV: workgroup = 8 waves for 128 keys; 64-row blocks of Q, dO and their references and D
-// go through LDS once for all of them, for every query head of the K/V head's group.  Waves 0-3
-// accumulate dV (from P), waves 4-7 dK (from dS), 32 keys each: a wave holds one accumulator set,
-// S is computed by both, and each SIMD pairs a dV wave with a heavier dK wave.
+// go through LDS once for all of them, for every query head of the K/V head's group.  Waves w and
+// w + 4 share 32 keys: wave w computes S = Q K^T, turns it into P and accumulates dV^T += dO^T P;
+// wave w + 4 computes dP = dO V^T, takes P from wave w through LDS and accumulates
+// dK^T += Q^T dS.  So every wave runs two of the four products per block and holds one operand
+// set and one accumulator set, and the two waves of a SIMD carry equal loads.  The dK waves work
+// one block behind the dV waves (the P of block t is read in step t + 1), so one barrier per step
+// orders everything: Q / dO / reference blocks are triple-buffered, P double-buffered.
 template <bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -246,34 +250,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, int nkt, float scale,
     float scale_log2) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ql0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t ql1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t gl0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t gl1[TILE];
-  __shared__ __attribute__((aligned(16))) float sl0[2 * BT];  // reference (log2 units), then D
-  __shared__ __attribute__((aligned(16))) float sl1[2 * BT];
+  __shared__ __attribute__((aligned(1024))) uint16_t qls[3][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t gls[3][TILE];
+  __shared__ __attribute__((aligned(16))) float sls[3][2 * BT];  // reference (log2 units), then D
+  // P of each wave pair as packed bf16 operands: [buffer][pair][operand i][lane], 16 bytes each,
+  // so that a wave's 16-byte stores and loads of one operand cover 1 KB contiguously
+  __shared__ __attribute__((aligned(1024))) u32x4 pls[2][4 * 4 * 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const bool do_k = wave >= 4;
+  const int pair = wave & 3;
   const int BHk = gridDim.x / nkt;
   const int bhk = blockIdx.x % BHk, kt = blockIdx.x / BHk;
   const int b = bhk / Hkv, hkv = bhk - b * Hkv, G = Hq / Hkv;
   const int off = Nk - Nq;
-  const int kw0 = kt * 128 + (wave & 3) * 32, my_k = kw0 + l32;
+  const int kw0 = kt * 128 + pair * 32, my_k = kw0 + l32;
 
-  // K (and for dK, V) of this lane's key as the B operand
-  u32x4 kf[NCB], vf[NCB];
+  // this lane's key row as the B operand of the wave's first product: K (for S) or V (for dP)
+  u32x4 bf[NCB];
   {
     const bool ok = my_k < Nk;
-    const uint16_t* krow = K + ((size_t)bhk * Nk + min(my_k, Nk - 1)) * BD;
-    const uint16_t* vrow = V + ((size_t)bhk * Nk + min(my_k, Nk - 1)) * BD;
+    const uint16_t* row = (do_k ? V : K) + ((size_t)bhk * Nk + min(my_k, Nk - 1)) * BD;
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-      kf[c] = ok ? *(const u32x4*)(krow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
-      vf[c] = ok && do_k ? *(const u32x4*)(vrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int c = 0; c < NCB; ++c)
+      bf[c] = ok ? *(const u32x4*)(row + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
   }
 
   // query blocks that see any key of this workgroup: rows q with q + off >= kt * 128
@@ -282,18 +284,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int per_head = max(0, nqb - qb0);
   const int n_steps = G * per_head;
 
-  auto stage = [&](int step, uint16_t* qd, uint16_t* gd, float* sd) {
+  auto stage = [&](int step, int buf) {
     const int g = step / per_head, qb = qb0 + step - g * per_head;
     const size_t bh = (size_t)b * Hq + hkv * G + g;
     if (wave < 4)  // waves 0-3 copy the Q block, waves 4-7 the dO block
-      copy_tile(Q + bh * Nq * BD, qb * BT, Nq, qd, wave, lane);
+      copy_tile(Q + bh * Nq * BD, qb * BT, Nq, qls[buf], wave, lane);
     else
-      copy_tile(dO + bh * Nq * BD, qb * BT, Nq, gd, wave - 4, lane);
+      copy_tile(dO + bh * Nq * BD, qb * BT, Nq, gls[buf], wave - 4, lane);
     if (wave == 0) {  // 64 references then 64 D, four bytes per lane; rows past Nq read zero
       const int q = qb * BT;
       const uint32_t n = (uint32_t)max(0, Nq - q) * 4;
-      load_lds_4(make_rsrc(L2 + bh * Nq + min(q, Nq), n), sd, (uint32_t)lane * 4);
-      load_lds_4(make_rsrc(Dd + bh * Nq + min(q, Nq), n), sd + BT, (uint32_t)lane * 4);
+      load_lds_4(make_rsrc(L2 + bh * Nq + min(q, Nq), n), sls[buf], (uint32_t)lane * 4);
+      load_lds_4(make_rsrc(Dd + bh * Nq + min(q, Nq), n), sls[buf] + BT, (uint32_t)lane * 4);
     }
   };
 
@@ -302,67 +304,81 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 
-  if (n_steps > 0) stage(0, ql0, gl0, sl0);
-  for (int t = 0; t < n_steps; ++t) {
-    const uint16_t* qc = (t & 1) ? ql1 : ql0;
-    const uint16_t* gc = (t & 1) ? gl1 : gl0;
-    const float* sc = (t & 1) ? sl1 : sl0;
+  if (n_steps > 0) stage(0, 0);
+  // step t: the dV waves take block t (buffer t % 3), the dK waves block t - 1
+  for (int t = 0, bc = 0; t <= n_steps; ++t, bc = bc == 2 ? 0 : bc + 1) {
     wait_vmem();
-    __syncthreads();  // step t's blocks are in LDS; the other buffers are free
-    if (t + 1 < n_steps) stage(t + 1, (t & 1) ? ql0 : ql1, (t & 1) ? gl0 : gl1, (t & 1) ? sl0 : sl1);
-    const int qb = qb0 + t % per_head;
-    const int q0 = qb * BT;
+    __syncthreads();  // block t is in LDS, so is the P of block t - 1; buffer (t + 1) % 3 is free
+    if (t + 1 < n_steps) stage(t + 1, bc == 2 ? 0 : bc + 1);
+    const int blk = do_k ? t - 1 : t;
+    if (blk < 0 || blk >= n_steps) continue;
+    const int bb = do_k ? (bc == 0 ? 2 : bc - 1) : bc;
+    const uint16_t* qc = qls[bb];
+    const uint16_t* gc = gls[bb];
+    const float* sc = sls[bb];
+    u32x4* const pw = pls[blk & 1] + pair * 4 * 64 + lane;  // this lane's operand slots (stride 64)
+    const int q0 = (qb0 + blk % per_head) * BT;
     if (kw0 >= Nk || (CAUSAL && q0 + BT - 1 + off < kw0)) continue;  // nothing visible
-    // S = Q K^T (and for dK, dP = dO V^T) for both 32-row halves, the independent products
-    // interleaved: half j holds queries q0 + 32 j + 8 (r >> 2) + 4 h + (r & 3) of this key.
-    u32x4 pb[4];  // P (for dV) or dS (for dK) as the B operand, 16 queries each
-    auto finish_half = [&](int half, const f32x16& sh, const f32x16& dph) {
-      const int qh0 = q0 + 32 * half;
-      const bool need = (qh0 + 32 > Nq) || (kw0 + 32 > Nk) || (CAUSAL && kw0 + 31 > qh0 + off);
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int qi = 32 * half + 8 * g4 + 4 * h;  // first of this lane's four rows
-        const f32x4 l4 = *(const f32x4*)(sc + qi);
-        const f32x4 d4 = *(const f32x4*)(sc + BT + qi);
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const int r = 4 * g4 + e;
-          float s0 = sh[r], s1 = sh[r + 1], d0 = dph[r], d1 = dph[r + 1];
-          // (rows past Nq read a reference of 0 and are masked below)
-          p_and_ds(s0, d0, scale_log2, l4[e], d4[e]);
-          p_and_ds(s1, d1, scale_log2, l4[e + 1], d4[e + 1]);
-          if (need) {
-            const int q = q0 + qi + e;
-            const bool ok0 = q < Nq && my_k < Nk && (!CAUSAL || my_k <= q + off);
-            const bool ok1 = q + 1 < Nq && my_k < Nk && (!CAUSAL || my_k <= q + 1 + off);
-            if (!ok0) s0 = d0 = 0.f;
-            if (!ok1) s1 = d1 = 0.f;
-          }
-          const int j = 16 * half + r;
-          pb[j >> 3][(j >> 1) & 3] = do_k ? pack_bf16x2(d0, d1) : pack_bf16x2(s0, s1);
-        }
-      }
-    };
-    if (do_k) {
-      f32x16 s2[2] = {f32x16{}, f32x16{}}, d2[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int c = 0; c < NCB; ++c)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          s2[half] = mfma32x32x16(read_row(qc, tl.row_base, half, c), kf[c], s2[half]);
-          d2[half] = mfma32x32x16(read_row(gc, tl.row_base, half, c), vf[c], d2[half]);
-        }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) finish_half(half, s2[half], d2[half]);
-    } else {
-      f32x16 s2[2] = {f32x16{}, f32x16{}};
+    // first product for both 32-row halves, interleaved: S = Q K^T or dP = dO V^T; half j holds
+    // queries q0 + 32 j + 8 (r >> 2) + 4 h + (r & 3) of this key
+    f32x16 r2[2] = {f32x16{}, f32x16{}};
+    {
+      const uint16_t* xa = do_k ? gc : qc;
 #pragma unroll
       for (int c = 0; c < NCB; ++c)
 #pragma unroll
         for (int half = 0; half < 2; ++half)
-          s2[half] = mfma32x32x16(read_row(qc, tl.row_base, half, c), kf[c], s2[half]);
+          r2[half] = mfma32x32x16(read_row(xa, tl.row_base, half, c), bf[c], r2[half]);
+    }
+    u32x4 pb[4];  // P (dV) or dS (dK) as the B operand of the second product, 16 queries each
+    if (!do_k) {
+      // P = 2^(S scale log2e - reference), zero outside the causal / valid range, published for
+      // the pair's dK wave
 #pragma unroll
-      for (int half = 0; half < 2; ++half) finish_half(half, s2[half], f32x16{});
+      for (int half = 0; half < 2; ++half) {
+        const int qh0 = q0 + 32 * half;
+        const bool need = (qh0 + 32 > Nq) || (kw0 + 32 > Nk) || (CAUSAL && kw0 + 31 > qh0 + off);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qi = 32 * half + 8 * g4 + 4 * h;  // first of this lane's four rows
+          const f32x4 l4 = *(const f32x4*)(sc + qi);
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const int r = 4 * g4 + e;
+            // (rows past Nq read a reference of 0 and are masked below)
+            float p0 = fast_exp2(fmaf(r2[half][r], scale_log2, -l4[e]));
+            float p1 = fast_exp2(fmaf(r2[half][r + 1], scale_log2, -l4[e + 1]));
+            if (need) {
+              const int q = q0 + qi + e;
+              if (!(q < Nq && my_k < Nk && (!CAUSAL || my_k <= q + off))) p0 = 0.f;
+              if (!(q + 1 < Nq && my_k < Nk && (!CAUSAL || my_k <= q + 1 + off))) p1 = 0.f;
+            }
+            const int j = 16 * half + r;
+            pb[j >> 3][(j >> 1) & 3] = pack_bf16x2(p0, p1);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[64 * i] = pb[i];
+    } else {
+      // dS = P (dP - D) from the pair's P of this block (zero wherever the pair is masked)
+      u32x4 pw4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw4[i] = pw[64 * i];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 d4 = *(const f32x4*)(sc + BT + 32 * half + 8 * g4 + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const int r = 4 * g4 + e, j = 16 * half + r;
+            const uint32_t w = pw4[j >> 3][(j >> 1) & 3];
+            pb[j >> 3][(j >> 1) & 3] =
+                pack_bf16x2(__uint_as_float(w << 16) * (r2[half][r] - d4[e]),
+                            __uint_as_float(w & 0xffff0000u) * (r2[half][r + 1] - d4[e + 1]));
+          }
+        }
     }
     // dK^T += Q^T dS or dV^T += dO^T P, 16 queries at a time
     const uint16_t* at = do_k ? qc : gc;
