@@ -380,13 +380,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           }
         }
     }
-    // dK^T += Q^T dS or dV^T += dO^T P, 16 queries at a time
+    // dK^T += Q^T dS or dV^T += dO^T P, 16 queries at a time, at raised priority so that the
+    // SIMD's other wave fills the gaps between these products with its vector work
     const uint16_t* at = do_k ? qc : gc;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         acc[db] = mfma32x32x16(read_tr(at, tl.tr_base, 16 * g, db), pb[g], acc[db]);
+    __builtin_amdgcn_s_setprio(0);
   }
   if (my_k < Nk)
     store_rowT((do_k ? dK : dV) + ((size_t)bhk * Nk + my_k) * BD, acc, do_k ? scale : 1.f, h);

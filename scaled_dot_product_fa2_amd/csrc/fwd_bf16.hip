@@ -438,8 +438,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 
     // Oᵀ += Vᵀ·Pᵀ, 16-key group by group (group g is operand pb[g]); while group g's products
     // run, group g+1's exponentials and group g's row sums are done.  V operands of group g+1
-    // are read while group g's products run.
+    // are read while group g's products run.  The wave issues this part at raised priority: the
+    // SIMD's other wave, in the vector-heavy first part of its own step, then fills the gaps
+    // between these products instead of delaying them (measured 3-7% on multi-round grids).
     constexpr int NDB = D / 32;
+    __builtin_amdgcn_s_setprio(1);
     float rs = 0.f;
     bf16x8 vop[2][NDB];
 #pragma unroll
@@ -464,6 +467,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     l_run += rs;  // lane-half partial; the partner half is added at the end
   };
 
