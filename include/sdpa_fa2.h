@@ -58,12 +58,12 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
   ATTN_ERR_SHAPE = -2,     /* a negative dimension, a size that overflows, or a too-long K/V */
-  ATTN_ERR_HEADDIM = -3,   /* d is not 64 or 128 */
+  ATTN_ERR_HEADDIM = -3,   /* d is not 64 or 128 (attn_bwd: not 128) */
   ATTN_ERR_GQA = -4,       /* Hkv < 1 while Hq > 0, or Hq % Hkv != 0 */
   ATTN_ERR_ALIGN = -5,     /* a tensor base address is not suitably aligned */
   ATTN_ERR_SCALE = -6,     /* scale is negative, NaN or infinite */
   ATTN_ERR_SPLITS = -7,    /* n_splits < 1 or n_splits > max(Nk, 1) */
-  ATTN_ERR_WORKSPACE = -8, /* workspace NULL or smaller than attn_decode_workspace_bytes() */
+  ATTN_ERR_WORKSPACE = -8, /* workspace NULL or smaller than its *_workspace_bytes() size */
   ATTN_ERR_LAUNCH = -9,    /* the HIP runtime rejected a kernel launch */
   ATTN_ERR_BIAS = -10      /* bias_b not 1 or B, bias_h not 1 or Hq, or Nk % 4 != 0 with a bias */
 };

@@ -257,12 +257,13 @@ const char* attn_status_string(int status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid shape: negative dimension or size overflow";
-    case ATTN_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
+    case ATTN_ERR_HEADDIM:
+      return "unsupported head dimension (64 or 128; the backward takes 128 only)";
     case ATTN_ERR_GQA: return "Hq must be a positive multiple of Hkv";
     case ATTN_ERR_ALIGN: return "tensor base address is not suitably aligned";
     case ATTN_ERR_SCALE: return "scale must be finite and >= 0 (0 selects 1/sqrt(d))";
     case ATTN_ERR_SPLITS: return "n_splits must be in [1, max(Nk, 1)]";
-    case ATTN_ERR_WORKSPACE: return "decode workspace is NULL or too small";
+    case ATTN_ERR_WORKSPACE: return "workspace is NULL or too small";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
     case ATTN_ERR_BIAS:
       return "bias dims must be 1 or B (batch) and 1 or Hq (heads), and Nk a multiple of 4";
