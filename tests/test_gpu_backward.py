@@ -96,6 +96,29 @@ def test_backward_long_causal():
         _check(name, a, r)
 
 
+def test_backward_bench_shape_sampled_heads():
+    # the launch the backward benchmark times (B2 H16 N2048 causal, all heads in one call); the
+    # oracle differentiates four whole (batch, head) slices of it
+    w = I.WORKLOADS["prefill_causal_b2h16n2048"]
+    x = w.draw()
+    g_bits = I.draw_grad(w.seed + 4300, (w.B, w.Hq, w.Nq, w.d))
+    q, k, v = upload(x)
+    dout = I.to_device(g_bits, "bf16")
+    s32 = _s32(w.d)
+    say("backward B2 H16 N2048 causal, sampled heads")
+    out, lse = fa.attn_fwd(q, k, v, causal=True, scale=s32)
+    dq, dk, dv = fa.attn_bwd(q, k, v, out, lse, dout, causal=True, scale=s32)
+    torch.cuda.synchronize()
+    got = [to_f64(t) for t in (dq, dk, dv)]
+    qf, kf, vf = x.as_f64()
+    g = I.bf16_bits_to_f32(g_bits).astype(np.float64)
+    for b, hh in ((0, 0), (0, 15), (1, 7), (1, 12)):
+        sl = (slice(b, b + 1), slice(hh, hh + 1))
+        ref = A.attention_backward_fp64(qf[sl], kf[sl], vf[sl], g[sl], s32, True)
+        for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+            _check(f"{name}[{b},{hh}]", a[sl], r)
+
+
 def test_backward_deterministic_and_fully_written():
     got, _, (q, k, v, out, lse, dout) = _run(2, 4, 2, 200, 333, True, seed=4200)
     s32 = _s32(128)
