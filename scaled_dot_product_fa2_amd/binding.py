@@ -123,6 +123,40 @@ def _validate(q, k, v, dtype):
     return B, Hq, k.shape[1], Nq, k.shape[2], d
 
 
+def _check_like(name, t, shape, dtype, device):
+    """A caller-supplied output or workspace must match exactly what the kernels will write."""
+    import torch
+
+    if (not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(shape) or
+            t.device != device or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on "
+                         f"{device}")
+    return t
+
+
+def _out_lse(q, B, Hq, Nq, out, lse, want_lse):
+    """The output and logsumexp tensors: allocated when not given, checked when given."""
+    import torch
+
+    out = torch.empty_like(q) if out is None else _check_like("out", out, q.shape, q.dtype,
+                                                              q.device)
+    if lse is None:
+        if want_lse:
+            lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    else:
+        lse = _check_like("lse", lse, (B, Hq, Nq), torch.float32, q.device)
+    return out, lse
+
+
+def _check_workspace(workspace, device):
+    import torch
+
+    if (not isinstance(workspace, torch.Tensor) or workspace.device != device or
+            not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return workspace
+
+
 def _extras(q, B, Hq, Nq, Nk, seqlens_k, bias):
     """Marshal the optional per-batch key lengths (int32 [B]) and bias (bf16 [1|B, 1|Hq, Nq, Nk])
     into (seqlens_ptr, bias_ptr, bias_b, bias_h); shape rules beyond these are the library's."""
@@ -151,10 +185,7 @@ def attn_fwd(q, k, v, causal: bool = True, scale: float = 0.0, out=None, lse=Non
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out, lse = _out_lse(q, B, Hq, Nq, out, lse, want_lse)
     rc = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                          float(scale), int(bool(causal)), _stream(q.device))
     _check_rc(rc, "attn_fwd")
@@ -169,10 +200,7 @@ def attn_fwd_ex(q, k, v, causal: bool = True, scale: float = 0.0, seqlens_k=None
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
     sp, bp, bb, bh = _extras(q, B, Hq, Nq, Nk, seqlens_k, bias)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out, lse = _out_lse(q, B, Hq, Nq, out, lse, want_lse)
     rc = load().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), sp, bp, bb, bh, B, Hq,
                             Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(q.device))
     _check_rc(rc, "attn_fwd_ex")
@@ -185,10 +213,7 @@ def attn_fwd_f32(q, k, v, causal: bool = True, scale: float = 0.0, out=None, lse
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.float32)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out, lse = _out_lse(q, B, Hq, Nq, out, lse, want_lse)
     rc = load().attn_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq,
                              Nk, d, float(scale), int(bool(causal)), _stream(q.device))
     _check_rc(rc, "attn_fwd_f32")
@@ -213,10 +238,8 @@ def attn_decode_splitkv(q, k, v, n_splits: int, causal: bool = True, scale: floa
     need = attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits) if n_splits >= 1 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_workspace(workspace, q.device)
+    out, lse = _out_lse(q, B, Hq, Nq, out, lse, want_lse)
     rc = load().attn_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
@@ -237,10 +260,8 @@ def attn_decode_splitkv_ex(q, k, v, n_splits: int, causal: bool = True, scale: f
     need = attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits) if n_splits >= 1 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_workspace(workspace, q.device)
+    out, lse = _out_lse(q, B, Hq, Nq, out, lse, want_lse)
     rc = load().attn_decode_splitkv_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                        _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), sp, bp, bb,
@@ -269,10 +290,9 @@ def attn_forward(q, k, v, causal: bool = True, scale: float = 0.0, seqlens_k=Non
     need = attn_forward_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and want_lse:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if workspace is not None:
+        _check_workspace(workspace, q.device)
+    out, lse = _out_lse(q, B, Hq, Nq, out, lse, want_lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load().attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
                              ws_bytes, sp, bp, bb, bh, B, Hq, Hkv, Nq, Nk, d, float(scale),
@@ -295,12 +315,13 @@ def attn_bwd(q, k, v, out, lse, dout, causal: bool = True, scale: float = 0.0, d
     if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or
             tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous() or lse.device != q.device):
         raise ValueError("lse must be the forward's contiguous float32 [B, Hq, Nq] logsumexp")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q) if dq is None else _check_like("dq", dq, q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else _check_like("dk", dk, k.shape, k.dtype, q.device)
+    dv = torch.empty_like(v) if dv is None else _check_like("dv", dv, v.shape, v.dtype, q.device)
     need = attn_bwd_workspace_bytes(B, Hq, Nq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q.device)
     rc = load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
                          _ptr(dk), _ptr(dv), _ptr(workspace),
                          workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
@@ -319,6 +340,11 @@ def prepare_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, causal: bool = T
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    for name, t, ref in (("out", out, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k),
+                         ("dv", dv, v)):
+        _check_like(name, t, ref.shape, ref.dtype, q.device)
+    _check_like("lse", lse, (B, Hq, Nq), torch.float32, q.device)
+    _check_workspace(workspace, q.device)
     fn = load().attn_bwd
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
             _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq, Hkv,
@@ -339,6 +365,9 @@ def prepare_fwd(q, k, v, out, lse=None, causal: bool = True, scale: float = 0.0,
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_like("lse", lse, (B, Hq, Nq), torch.float32, q.device)
     tail = (B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(q.device))
     if seqlens_k is None and bias is None:
         fn, name = load().attn_fwd, "attn_fwd"
@@ -361,6 +390,10 @@ def prepare_decode(q, k, v, n_splits: int, out, lse, workspace, causal: bool = T
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    _check_like("out", out, q.shape, q.dtype, q.device)
+    if lse is not None:
+        _check_like("lse", lse, (B, Hq, Nq), torch.float32, q.device)
+    _check_workspace(workspace, q.device)
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
             workspace.numel() * workspace.element_size())
     tail = (B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(n_splits),

@@ -184,3 +184,24 @@ def test_invalid_arguments_raise_before_launch():
         fa.attn_fwd(q, k, k)
     with pytest.raises(fa.AttentionError, match="scale"):
         fa.attn_fwd(k, k, k, scale=float("nan"))
+
+
+def test_binding_rejects_mismatched_outputs():
+    # caller-supplied outputs, gradients and workspaces must match what the kernels write; the
+    # binding refuses anything else before a launch
+    q = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16, device="cuda")
+    bad_out = torch.empty((1, 2, 32, 128), dtype=torch.bfloat16, device="cuda")
+    bad_lse = torch.empty((1, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError, match="out must be"):
+        fa.attn_fwd(q, q, q, out=bad_out)
+    with pytest.raises(ValueError, match="lse must be"):
+        fa.attn_fwd(q, q, q, lse=bad_lse)
+    with pytest.raises(ValueError, match="out must be"):
+        fa.prepare_fwd(q, q, q, bad_out)
+    with pytest.raises(ValueError, match="workspace must be"):
+        fa.attn_decode_splitkv(q, q, q, 2, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    out, lse = fa.attn_fwd(q, q, q)
+    with pytest.raises(ValueError, match="dk must be"):
+        fa.attn_bwd(q, q, q, out, lse, q, dk=torch.empty((1, 2, 64, 64), dtype=torch.bfloat16,
+                                                         device="cuda"))
+    torch.cuda.synchronize()
