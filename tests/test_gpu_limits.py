@@ -115,3 +115,67 @@ def test_one_more_key_is_rejected():
     rc = lib.attn_fwd(q.data_ptr(), q.data_ptr(), q.data_ptr(), q.data_ptr(), None, 1, 1, 1, 1,
                       NK_MAX + 1, D, 0.0, 1, None)
     assert rc == -2  # ATTN_ERR_SHAPE, before anything is launched
+
+
+def test_backward_at_the_maximum_key_length(big_kv):
+    """Gradients at 2^24 - 129 keys (GQA: two query heads, one K/V head; Nq = 64 causal, so row i
+    sees every ordinary key and the first i + 1 special keys).  With dO = g·1 every head
+    contributes the same, and the chain rule of the closed form gives, per row i
+    (P_ord = 1/den_i, P_sp = E/den_i, E = e^S, dP = 128 g v, D_i = 128 g O_i):
+        dV_j = 2 g Σ_i P_ij,   dK_j = 2 scale c e0 Σ_i P_ij (dP_j - D_i),
+        dQ_i = scale β e0 Σ_{special j ≤ i + off} P_ij (dP_j - D_i).
+    The 16.7 million ordinary keys must all get bit-identical gradients (checked on the GPU);
+    one of them, every special key and every dQ row are compared with the closed form."""
+    k, v = big_kv
+    Hq, Nq, g = 2, 64, 0.25
+    q = torch.zeros((1, Hq, Nq, D), dtype=torch.bfloat16, device="cuda")
+    q[..., 0] = C_Q
+    dout = torch.full((1, Hq, Nq, D), g, dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    s32 = float(np.float32(scale))
+    say(f"backward Nq={Nq} Nk={NK_MAX}")
+    out, lse = fa.attn_fwd(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = fa.attn_bwd(q, k, v, out, lse, dout, causal=True, scale=scale)
+    torch.cuda.synchronize()
+
+    # closed form, fp64
+    E = math.exp(s32 * C_Q * BETA)
+    n_ord = NK_MAX - N_SPECIAL
+    i = np.arange(Nq)
+    m = i + 1                                   # special keys row i sees
+    den = n_ord + m * E
+    O = (n_ord * V0 + m * E * V1) / den
+    Drow = 128 * g * O
+    dp_ord, dp_sp = 128 * g * V0, 128 * g * V1
+    dv_ord = Hq * g * np.sum(1.0 / den)
+    dk_ord = Hq * s32 * C_Q * np.sum((dp_ord - Drow) / den)
+    sp = np.arange(N_SPECIAL)                   # special key s is seen by rows i >= s
+    vis = i[None, :] >= sp[:, None]
+    dv_sp = Hq * g * np.sum(np.where(vis, E / den[None, :], 0.0), axis=1)
+    dk_sp = Hq * s32 * C_Q * np.sum(np.where(vis, E * (dp_sp - Drow[None, :]) / den[None, :], 0.0),
+                                    axis=1)
+    dq0 = s32 * BETA * m * E * (dp_sp - Drow) / den   # the same for both heads
+
+    # every ordinary key: identical gradients, dK only in dimension 0
+    ordv = dv[0, 0, :n_ord]  # bf16 views: min / max compare bits exactly without copies
+    ordk = dk[0, 0, :n_ord]
+    assert float(ordv.min()) == float(ordv.max()), "ordinary keys' dV differ"
+    assert float(ordk[:, 0].min()) == float(ordk[:, 0].max()), "ordinary keys' dK differ"
+    assert float(ordk[:, 1:].abs().max()) == 0.0
+    got_v, got_k = float(ordv[0, 0]), float(ordk[0, 0])
+    say(f"  ordinary dV {got_v:.6e} vs {dv_ord:.6e}, dK {got_k:.6e} vs {dk_ord:.6e}")
+    assert abs(got_v - dv_ord) <= 2e-2 * abs(dv_ord)
+    assert abs(got_k - dk_ord) <= 2e-2 * abs(dk_ord) + 1e-9
+
+    # the special keys and dQ, row by row (relative to each tensor's largest value)
+    gv = to_f64(dv[0, 0, n_ord:])
+    gk = to_f64(dk[0, 0, n_ord:])
+    gq = to_f64(dq[0])
+    for name, got, ref in (("dV special", gv, np.repeat(dv_sp[:, None], D, axis=1)),
+                           ("dK special", gk[:, 0], dk_sp),
+                           ("dQ", gq[:, :, 0], np.broadcast_to(dq0, (Hq, Nq)))):
+        scale_ref = float(np.abs(ref).max())
+        err = float(np.abs(got - ref).max()) / scale_ref
+        say(f"  {name}: max|ref|={scale_ref:.3e} max_rel={err:.3e}")
+        assert err <= 2e-2, name
+    assert float(np.abs(gk[:, 1:]).max()) == 0.0 and float(np.abs(gq[:, :, 1:]).max()) == 0.0
