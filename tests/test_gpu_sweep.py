@@ -106,3 +106,79 @@ def test_backward(case):
         assert np.all(np.isfinite(a)), name
         assert float(err.max()) / scale <= GRAD_MAX_REL, f"{name} {case}"
         assert float(err.mean()) / scale <= GRAD_MEAN_REL, f"{name} {case}"
+
+
+def _extras_draw(case, seed):
+    """Random per-batch key lengths and a random bias of a random broadcast shape for a case."""
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    rng = np.random.default_rng(seed)
+    L = I.draw_seqlens(seed + 1, B, Nk, edges=False) if rng.integers(0, 2) else None
+    bias_bits = None
+    if rng.integers(0, 3):  # two cases in three carry a bias
+        Bb = B if rng.integers(0, 2) else 1
+        Hb = Hq if rng.integers(0, 2) else 1
+        kind = "alibi" if rng.integers(0, 3) == 0 else "normal"
+        bias_bits = I.draw_bias(seed + 2, Bb, Hb, Nq, Nk, kind, std=float(rng.choice([1.0, 4.0])),
+                                masked_frac=float(rng.choice([0.0, 0.1])))
+    return L, bias_bits
+
+
+def _extras_case(c, nq_max=None):
+    # bias rows are 8-byte groups of four keys: Nk a multiple of 4
+    B, Hq, Hkv, Nq, Nk, d, causal = c
+    if nq_max is not None:
+        Nq = 1 + Nq % nq_max
+    return (B, Hq, Hkv, Nq, max(4, Nk - Nk % 4), d, causal)
+
+
+FWD_EX = [_extras_case(c) for c in _shapes(9400, 16)]
+DEC_EX = [_extras_case(c, 8) for c in _shapes(9500, 12)]
+
+
+def _ref(x, s32, causal, L, bias_bits):
+    return A.attention_fp64(*x.as_f64(), s32, causal, seqlens_k=L,
+                            bias=None if bias_bits is None else
+                            I.bf16_bits_to_f32(bias_bits).astype(np.float64))
+
+
+def _dev_extras(L, bias_bits):
+    return (None if L is None else torch.as_tensor(np.asarray(L, np.int32), device="cuda"),
+            None if bias_bits is None else I.to_device(bias_bits, "bf16"))
+
+
+@pytest.mark.parametrize("case", FWD_EX, ids=_ids)
+def test_forward_with_extras(case):
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    seed = 9400 + 11 * Nq + Nk
+    L, bias_bits = _extras_draw(case, seed)
+    x = I.draw_qkv(seed, B, Hq, Hkv, Nq, Nk, d)
+    q, k, v = upload(x)
+    sl, bias = _dev_extras(L, bias_bits)
+    say(f"sweep forward_ex {case} lens={None if L is None else list(L)} "
+        f"bias={None if bias_bits is None else bias_bits.shape}")
+    out, lse = fa.attn_fwd_ex(q, k, v, causal=causal, scale=_s32(d), seqlens_k=sl, bias=bias)
+    out2, lse2, _ = fa.attn_forward(q, k, v, causal=causal, scale=_s32(d), seqlens_k=sl, bias=bias)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = _ref(x, _s32(d), causal, L, bias_bits)
+    compare(to_f64(out), to_f64(lse), O_ref, lse_ref, BF16_MAX_ABS, BF16_MEAN_ABS, what=str(case))
+    compare(to_f64(out2), to_f64(lse2), O_ref, lse_ref, BF16_MAX_ABS, BF16_MEAN_ABS,
+            what=f"attn_forward {case}")
+
+
+@pytest.mark.parametrize("case", DEC_EX, ids=_ids)
+def test_decode_with_extras(case):
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    seed = 9500 + 13 * Nq + Nk
+    L, bias_bits = _extras_draw(case, seed)
+    n_splits = int(np.random.default_rng(seed).integers(1, min(Nk, 40) + 1))
+    x = I.draw_qkv(seed, B, Hq, Hkv, Nq, Nk, d)
+    q, k, v = upload(x)
+    sl, bias = _dev_extras(L, bias_bits)
+    say(f"sweep decode_ex {case} splits={n_splits} lens={None if L is None else list(L)} "
+        f"bias={None if bias_bits is None else bias_bits.shape}")
+    out, lse, _ = fa.attn_decode_splitkv_ex(q, k, v, n_splits, causal=causal, scale=_s32(d),
+                                            seqlens_k=sl, bias=bias)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = _ref(x, _s32(d), causal, L, bias_bits)
+    compare(to_f64(out), to_f64(lse), O_ref, lse_ref, BF16_MAX_ABS, BF16_MEAN_ABS,
+            what=f"decode_ex {case} splits={n_splits}")
