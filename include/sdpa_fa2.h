@@ -58,7 +58,7 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
   ATTN_ERR_SHAPE = -2,     /* a negative dimension, a size that overflows, or a too-long K/V */
-  ATTN_ERR_HEADDIM = -3,   /* d is not 64 or 128 (attn_bwd: not 128) */
+  ATTN_ERR_HEADDIM = -3,   /* d is not 64 or 128 */
   ATTN_ERR_GQA = -4,       /* Hkv < 1 while Hq > 0, or Hq % Hkv != 0 */
   ATTN_ERR_ALIGN = -5,     /* a tensor base address is not suitably aligned */
   ATTN_ERR_SCALE = -6,     /* scale is negative, NaN or infinite */
@@ -202,7 +202,7 @@ SDPA_FA2_API size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
 
 /*
  * attn_bwd -- gradients of the attention forward (attn_fwd), bfloat16 in and out, fp32
- * accumulation.  Head dimension 128 only.  Not on the pages (they only report the backward's
+ * accumulation, head dimension 64 or 128.  Not on the pages (they only report the backward's
  * speed): the gradients of L = sum(dout * out) by the chain rule through the forward's steps,
  *   D_i = sum_d dout_id out_id,  P = exp(scale * q.k - lse) (masked positions 0),
  *   dv = P^T dout,  dS = P * (dout v^T - D),  dq = scale * dS k,  dk = scale * dS^T q,
@@ -215,8 +215,8 @@ SDPA_FA2_API size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  *     caller: fp32 D [B, Hq, Nq], then lse * log2(e) [B, Hq, Nq] (+inf for -inf rows), both
  *     overwritten; calls that share it must be stream ordered.
  * scale and causal must be those of the forward call.  Keys that no query sees get dk = dv = 0;
- * with Nq == 0 and Nk > 0 the call writes zeros to dk and dv.  Errors as for attn_fwd (d other
- * than 128 is ATTN_ERR_HEADDIM; Nq, like Nk, must keep one head slice below 4 GiB).
+ * with Nq == 0 and Nk > 0 the call writes zeros to dk and dv.  Errors as for attn_fwd (Nq, like
+ * Nk, must keep one head slice below 4 GiB).
  */
 SDPA_FA2_API int attn_bwd(const void* q, const void* k, const void* v, const void* out,
              const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -303,8 +303,8 @@ def attn_forward(q, k, v, causal: bool = True, scale: float = 0.0, seqlens_k=Non
 
 def attn_bwd(q, k, v, out, lse, dout, causal: bool = True, scale: float = 0.0, dq=None, dk=None,
              dv=None, workspace=None):
-    """Gradients (dq, dk, dv) of the forward on bf16 [B,H,N,128] tensors, given the forward's
-    output and logsumexp and the gradient ``dout`` of the loss w.r.t. the output."""
+    """Gradients (dq, dk, dv) of the forward on bf16 [B,H,N,d] tensors (d 64 or 128), given the
+    forward's output and logsumexp and the gradient ``dout`` of the loss w.r.t. the output."""
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)

@@ -218,7 +218,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   if (Nq >= kMaxSeq || Nk >= kMaxSeq) return ATTN_ERR_SHAPE;
   uint64_t tmp;
   if (!numel4(B, Hq, Nq, d, &tmp) || !numel4(B, Hkv, Nk, d, &tmp)) return ATTN_ERR_SHAPE;
-  if (d != 128) return ATTN_ERR_HEADDIM;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
   if (((uint64_t)Nk + 128u) * (uint64_t)d * 2u > 0xffffffffull ||
       ((uint64_t)Nq + 128u) * (uint64_t)d * 2u > 0xffffffffull)
     return ATTN_ERR_SHAPE;
@@ -257,8 +257,7 @@ const char* attn_status_string(int status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid shape: negative dimension or size overflow";
-    case ATTN_ERR_HEADDIM:
-      return "unsupported head dimension (64 or 128; the backward takes 128 only)";
+    case ATTN_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
     case ATTN_ERR_GQA: return "Hq must be a positive multiple of Hkv";
     case ATTN_ERR_ALIGN: return "tensor base address is not suitably aligned";
     case ATTN_ERR_SCALE: return "scale must be finite and >= 0 (0 selects 1/sqrt(d))";

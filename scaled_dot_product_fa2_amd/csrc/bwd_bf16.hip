@@ -32,60 +32,93 @@
 namespace fa {
 namespace {
 
-constexpr int BD = 128;            // head dim
-constexpr int BT = 64;             // rows per streamed block (keys in dq, queries in dkdv)
-constexpr int TILE = BT * BD;      // bf16 elements of one block
-constexpr int NCB = BD / 16;       // 16-dim slices per product
+constexpr int BT = 64;  // rows per streamed block (keys in dq, queries in dkdv)
 
-__device__ __forceinline__ int jswz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// Tile geometry for head dimension D (64 or 128).  A block of BT rows is stored unpadded, rows of
+// 2D bytes, with 16-byte chunks XOR-swizzled so that both LDS read patterns are conflict-free on
+// the 64 banks:
+//   D = 128 (256-byte rows): chunk c of row r at c ^ ((r & 3) << 2 | (r >> 2) & 3);
+//   D = 64 (128-byte rows, two rows per 256-byte line of banks): c ^ rev3((r >> 1) & 7), rev3
+//   reversing three bits.
+// The row-wise operand reads take 16 consecutive rows at one chunk; the transposing reads take
+// 4 consecutive rows x 4 chunks per 32 lanes.  Row r + 8 differs from row r by chunk bit 1
+// (D = 128) or bit 0 (D = 64): the second read of a transposing pair XORs that in (R8 bytes).
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  static constexpr int RB = 2 * D;                      // bytes per row
+  static constexpr int TILE = BT * D;                   // bf16 elements of one block
+  static constexpr int NCB = D / 16;                    // 16-dim slices per product
+  static constexpr int NDB = D / 32;                    // 32-dim output tiles
+  static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  static constexpr int RPL = 1024 / RB;                 // rows per 1 KB copy
+  static constexpr int LPW = BT / RPL / 4;              // 1 KB copies per wave per block
+  static constexpr uint32_t R8 = D == 128 ? 32u : 16u;  // byte XOR from row r to row r + 8
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+  }
+};
 
-// The lane's byte offsets inside a swizzled [rows][128] tile.
-//   row_base: row-wise A operand (rows x dims): lane (l32, h) reads row l32, dims 16c + 8h .. +7;
-//     the address of slice c is row_base ^ (32 c); rows 32..63 are + 32 * 256 bytes.
+// The lane's byte offsets inside a swizzled [BT][D] tile.
+//   row_base: row-wise A operand (rows x dims): lane (l32, h) reads row l32, dims 16c + 8h .. +7
+//     (logical chunk 2c + h); the address of slice c is row_base ^ (32 c); rows 32..63 are
+//     + 32 RB bytes.
 //   tr_base: transposing A operand (dims x rows) for the key/query order of the C layout; the
 //     operand of dim block db over rows R + (0..7, 8..15) is read at
-//     ((tr_base ^ (64 db)) + R * 256) and ((tr_base ^ (64 db) ^ 32) + (R + 8) * 256), R = 16 g.
+//     ((tr_base ^ (64 db)) + R RB) and ((tr_base ^ (64 db) ^ R8) + (R + 8) RB), R = 16 g.
 struct TileLanes {
   uint32_t row_base, tr_base;
 };
+template <int D>
 __device__ __forceinline__ TileLanes tile_lanes(int lane) {
+  using G = Geo<D>;
   const int h = lane >> 5, l32 = lane & 31;
   const int tr_g = lane >> 4, tr_j = (lane & 15) >> 2, tr_t = lane & 3;
   const int r0 = 4 * h + tr_j, cl = 2 * (tr_g & 1) + (tr_t >> 1);
   TileLanes t;
-  t.row_base = (uint32_t)(l32 * 256 + 16 * (h ^ jswz(l32)));
-  t.tr_base = (uint32_t)(r0 * 256 + 16 * (cl ^ jswz(r0)) + 8 * (tr_t & 1));
+  t.row_base = (uint32_t)(l32 * G::RB + 16 * (h ^ G::swz(l32)));
+  t.tr_base = (uint32_t)(r0 * G::RB + 16 * (cl ^ G::swz(r0)) + 8 * (tr_t & 1));
   return t;
 }
+template <int D>
 __device__ __forceinline__ u32x4 read_row(const uint16_t* tile, uint32_t row_base, int half, int c) {
-  return *(const u32x4*)((const char*)tile + half * 32 * 256 + (row_base ^ (32u * c)));
+  return *(const u32x4*)((const char*)tile + half * 32 * Geo<D>::RB + (row_base ^ (32u * c)));
 }
+template <int D>
 __device__ __forceinline__ bf16x8 read_tr(const uint16_t* tile, uint32_t tr_base, int R, int db) {
+  using G = Geo<D>;
   const char* b = (const char*)tile;
   const uint32_t a = tr_base ^ (64u * db);
-  return lds_read_tr16_pair((const uint16_t*)(b + a + R * 256),
-                            (const uint16_t*)(b + (a ^ 32u) + (R + 8) * 256));
+  return lds_read_tr16_pair((const uint16_t*)(b + a + R * G::RB),
+                            (const uint16_t*)(b + (a ^ G::R8) + (R + 8) * G::RB));
 }
 
-// Copy rows [r0, r0 + 64) of a [n_rows][128] bf16 matrix into a swizzled LDS tile: 4 waves x
-// 4 loads of 1 KB (four rows each); rows at or past n_rows read as zero.  Load i of wave w fills
-// rows 4 (4 i + w) .. +3, so the swizzled chunk of a lane does not depend on i.
+// Copy rows [r0, r0 + BT) of a [n_rows][D] bf16 matrix into a swizzled LDS tile: 4 waves x LPW
+// loads of 1 KB (RPL rows each); rows at or past n_rows read as zero.  Load i of wave w fills
+// rows RPL (4 i + w) .. +RPL-1, so the swizzled chunk of a lane does not depend on i.
+template <int D>
 __device__ __forceinline__ void copy_tile(const uint16_t* g, int r0, int n_rows, uint16_t* dst,
                                           int wave, int lane) {
-  const uint32_t skip = (uint32_t)min(r0, n_rows) * (BD * 2);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g + (size_t)skip / 2, (uint32_t)n_rows * BD * 2 - skip);
-  const int ld_row = lane >> 4, ld_chunk = lane & 15;
-  const int row = wave * 4 + ld_row;
-  const uint32_t voff = (uint32_t)row * 256 + 16u * (ld_chunk ^ jswz(row));
+  using G = Geo<D>;
+  const uint32_t skip = (uint32_t)min(r0, n_rows) * G::RB;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(g + (size_t)skip / 2, (uint32_t)n_rows * G::RB - skip);
+  const int ld_row = lane / G::CPR, ld_chunk = lane % G::CPR;
+  const int row = wave * G::RPL + ld_row;
+  const uint32_t voff = (uint32_t)row * G::RB + 16u * (ld_chunk ^ G::swz(row));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load_lds_16(rs, dst + (4 * i + wave) * 512, voff, (uint32_t)i * 4096);
+  for (int i = 0; i < G::LPW; ++i)
+    load_lds_16(rs, dst + (4 * i + wave) * 512, voff, (uint32_t)i * 4096);
 }
 
 // bf16 stores of one lane's C-layout accumulators (dims x rows, lane = row): 32 dims per tile
-__device__ __forceinline__ void store_rowT(uint16_t* row_ptr, const f32x16 (&acc)[4], float mul,
-                                           int h) {
+template <int D>
+__device__ __forceinline__ void store_rowT(uint16_t* row_ptr, const f32x16 (&acc)[D / 32],
+                                           float mul, int h) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const u32x2 w = {pack_bf16x2(acc[db][4 * g4 + 0] * mul, acc[db][4 * g4 + 1] * mul),
@@ -94,20 +127,22 @@ __device__ __forceinline__ void store_rowT(uint16_t* row_ptr, const f32x16 (&acc
     }
 }
 
-// D[row] = sum_d dO[row][d] * O[row][d] (16 lanes per row, 8 dims each), and the row's
+// D[row] = sum_d dO[row][d] * O[row][d] (D/8 lanes per row, 8 dims each), and the row's
 // reference for P in log2 units, L2[row] = LSE[row] * log2(e), +inf for a row with no visible key
 // (LSE = -inf) so that every P of it is exactly 0.
+template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O,
                                                        const uint16_t* __restrict__ dO,
                                                        const float* __restrict__ LSE,
                                                        float* __restrict__ Dd,
                                                        float* __restrict__ L2, long long rows) {
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
+  constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per row, rows per workgroup
+  const long long row = (long long)blockIdx.x * RPB + (threadIdx.x / LPR);
+  const int sub = threadIdx.x % LPR;
   float acc = 0.f;
   if (row < rows) {
-    const u32x4 o = *(const u32x4*)(O + row * BD + 8 * sub);
-    const u32x4 g = *(const u32x4*)(dO + row * BD + 8 * sub);
+    const u32x4 o = *(const u32x4*)(O + row * D + 8 * sub);
+    const u32x4 g = *(const u32x4*)(dO + row * D + 8 * sub);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc += __uint_as_float(o[i] << 16) * __uint_as_float(g[i] << 16);
@@ -115,7 +150,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
     }
   }
 #pragma unroll
-  for (int m = 8; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, LPR);
   if (row < rows && sub == 0) {
     Dd[row] = acc;
     const float l = LSE[row];
@@ -133,12 +168,13 @@ __device__ __forceinline__ void p_and_ds(float& s, float& dp, float c, float lse
 
 // ---------------------------------------------------------------------------------------------
 // dQ: workgroup = 4 waves = 128 query rows; 64-key blocks of K and V through LDS.
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dQ,
     int Hq, int Hkv, int Nq, int Nk, int nqt, float scale, float scale_log2) {
+  constexpr int TILE = Geo<D>::TILE, NCB = Geo<D>::NCB, NDB = Geo<D>::NDB;
   __shared__ __attribute__((aligned(1024))) uint16_t kl0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t kl1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t vl0[TILE];
@@ -152,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int b = bh / Hq, hq = bh - b * Hq, hkv = hq / (Hq / Hkv);
   const int off = Nk - Nq;
   const int qw0 = qt * 128 + wave * 32, my_q = qw0 + l32;
-  const uint16_t* kg = K + (size_t)(b * Hkv + hkv) * Nk * BD;
-  const uint16_t* vg = V + (size_t)(b * Hkv + hkv) * Nk * BD;
+  const uint16_t* kg = K + (size_t)(b * Hkv + hkv) * Nk * D;
+  const uint16_t* vg = V + (size_t)(b * Hkv + hkv) * Nk * D;
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(Nq - 1, qt * 128 + 127) + off + 1);
@@ -163,8 +199,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   u32x4 qf[NCB], gf[NCB];
   {
     const bool ok = my_q < Nq;
-    const uint16_t* qrow = Q + ((size_t)bh * Nq + min(my_q, Nq - 1)) * BD;
-    const uint16_t* grow = dO + ((size_t)bh * Nq + min(my_q, Nq - 1)) * BD;
+    const uint16_t* qrow = Q + ((size_t)bh * Nq + min(my_q, Nq - 1)) * D;
+    const uint16_t* grow = dO + ((size_t)bh * Nq + min(my_q, Nq - 1)) * D;
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
       qf[c] = ok ? *(const u32x4*)(qrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
@@ -178,14 +214,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     dd = Dd[(size_t)bh * Nq + my_q];
   }
 
-  const TileLanes tl = tile_lanes(lane);
-  f32x16 acc[4];
+  const TileLanes tl = tile_lanes<D>(lane);
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
   if (n_blk > 0) {
-    copy_tile(kg, 0, Nk, kl0, wave, lane);
-    copy_tile(vg, 0, Nk, vl0, wave, lane);
+    copy_tile<D>(kg, 0, Nk, kl0, wave, lane);
+    copy_tile<D>(vg, 0, Nk, vl0, wave, lane);
   }
   for (int t = 0; t < n_blk; ++t) {
     const uint16_t* kc = (t & 1) ? kl1 : kl0;
@@ -193,8 +229,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     wait_vmem();
     __syncthreads();  // block t is in LDS; the other buffers are free
     if (t + 1 < n_blk) {
-      copy_tile(kg, (t + 1) * BT, Nk, (t & 1) ? kl0 : kl1, wave, lane);
-      copy_tile(vg, (t + 1) * BT, Nk, (t & 1) ? vl0 : vl1, wave, lane);
+      copy_tile<D>(kg, (t + 1) * BT, Nk, (t & 1) ? kl0 : kl1, wave, lane);
+      copy_tile<D>(vg, (t + 1) * BT, Nk, (t & 1) ? vl0 : vl1, wave, lane);
     }
     if (qw0 >= Nq || (CAUSAL && t * BT > qw0 + 31 + off)) continue;
     // S^T = K Q^T and dP^T = V dO^T, 32 keys at a time (keys 32 kb + 8 (r >> 2) + 4 h + (r & 3)
@@ -208,8 +244,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
-        s = mfma32x32x16(read_row(kc, tl.row_base, kb, c), qf[c], s);
-        dp = mfma32x32x16(read_row(vc, tl.row_base, kb, c), gf[c], dp);
+        s = mfma32x32x16(read_row<D>(kc, tl.row_base, kb, c), qf[c], s);
+        dp = mfma32x32x16(read_row<D>(vc, tl.row_base, kb, c), gf[c], dp);
       }
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
@@ -229,9 +265,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = mfma32x32x16(read_tr(kc, tl.tr_base, 16 * g, db), pb[g], acc[db]);
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = mfma32x32x16(read_tr<D>(kc, tl.tr_base, 16 * g, db), pb[g], acc[db]);
   }
-  if (my_q < Nq) store_rowT(dQ + ((size_t)bh * Nq + my_q) * BD, acc, scale, h);
+  if (my_q < Nq) store_rowT<D>(dQ + ((size_t)bh * Nq + my_q) * D, acc, scale, h);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -243,13 +280,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 // set and one accumulator set, and the two waves of a SIMD carry equal loads.  The dK waves work
 // one block behind the dV waves (the P of block t is read in step t + 1), so one barrier per step
 // orders everything: Q / dO / reference blocks are triple-buffered, P double-buffered.
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, int nkt, float scale,
     float scale_log2) {
+  constexpr int TILE = Geo<D>::TILE, NCB = Geo<D>::NCB, NDB = Geo<D>::NDB;
   __shared__ __attribute__((aligned(1024))) uint16_t qls[3][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gls[3][TILE];
   __shared__ __attribute__((aligned(16))) float sls[3][2 * BT];  // reference (log2 units), then D
@@ -272,7 +310,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   u32x4 bf[NCB];
   {
     const bool ok = my_k < Nk;
-    const uint16_t* row = (do_k ? V : K) + ((size_t)bhk * Nk + min(my_k, Nk - 1)) * BD;
+    const uint16_t* row = (do_k ? V : K) + ((size_t)bhk * Nk + min(my_k, Nk - 1)) * D;
 #pragma unroll
     for (int c = 0; c < NCB; ++c)
       bf[c] = ok ? *(const u32x4*)(row + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
@@ -288,9 +326,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const int g = step / per_head, qb = qb0 + step - g * per_head;
     const size_t bh = (size_t)b * Hq + hkv * G + g;
     if (wave < 4)  // waves 0-3 copy the Q block, waves 4-7 the dO block
-      copy_tile(Q + bh * Nq * BD, qb * BT, Nq, qls[buf], wave, lane);
+      copy_tile<D>(Q + bh * Nq * D, qb * BT, Nq, qls[buf], wave, lane);
     else
-      copy_tile(dO + bh * Nq * BD, qb * BT, Nq, gls[buf], wave - 4, lane);
+      copy_tile<D>(dO + bh * Nq * D, qb * BT, Nq, gls[buf], wave - 4, lane);
     if (wave == 0) {  // 64 references then 64 D, four bytes per lane; rows past Nq read zero
       const int q = qb * BT;
       const uint32_t n = (uint32_t)max(0, Nq - q) * 4;
@@ -299,10 +337,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
   };
 
-  const TileLanes tl = tile_lanes(lane);
-  f32x16 acc[4];  // dK^T or dV^T of this wave's keys
+  const TileLanes tl = tile_lanes<D>(lane);
+  f32x16 acc[NDB];  // dK^T or dV^T of this wave's keys
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
 
   if (n_steps > 0) stage(0, 0);
   // step t: the dV waves take block t (buffer t % 3), the dK waves block t - 1
@@ -328,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       for (int c = 0; c < NCB; ++c)
 #pragma unroll
         for (int half = 0; half < 2; ++half)
-          r2[half] = mfma32x32x16(read_row(xa, tl.row_base, half, c), bf[c], r2[half]);
+          r2[half] = mfma32x32x16(read_row<D>(xa, tl.row_base, half, c), bf[c], r2[half]);
     }
     u32x4 pb[4];  // P (dV) or dS (dK) as the B operand of the second product, 16 queries each
     if (!do_k) {
@@ -387,34 +425,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        acc[db] = mfma32x32x16(read_tr(at, tl.tr_base, 16 * g, db), pb[g], acc[db]);
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = mfma32x32x16(read_tr<D>(at, tl.tr_base, 16 * g, db), pb[g], acc[db]);
     __builtin_amdgcn_s_setprio(0);
   }
   if (my_k < Nk)
-    store_rowT((do_k ? dK : dV) + ((size_t)bhk * Nk + my_k) * BD, acc, do_k ? scale : 1.f, h);
+    store_rowT<D>((do_k ? dK : dV) + ((size_t)bhk * Nk + my_k) * D, acc, do_k ? scale : 1.f, h);
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, const void* out, const float* lse,
                   const void* dout, void* dq, void* dk, void* dv, float* ws_d, const AttnShape& s,
                   float scale, hipStream_t stream) {
   const long long rows = (long long)s.B * s.Hq * s.Nq;
   float* const ws_l2 = ws_d + rows;  // the workspace holds D, then the log2-unit references
   const int nqt = (s.Nq + 127) / 128, nkt = (s.Nk + 127) / 128;
-  const long long g_prep = (rows + 15) / 16;
+  constexpr int RPB = 256 / (D / 8);  // rows per prep workgroup
+  const long long g_prep = (rows + RPB - 1) / RPB;
   const long long g_dq = (long long)s.B * s.Hq * nqt, g_kv = (long long)s.B * s.Hkv * nkt;
   if (g_prep > 0x7fffffffLL || g_dq > 0x7fffffffLL || g_kv > 0x7fffffffLL)
     return hipErrorInvalidConfiguration;
   hipError_t e = hipSuccess;
   if (g_prep > 0) {
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)g_prep), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)g_prep), dim3(256), 0, stream,
                        (const uint16_t*)out, (const uint16_t*)dout, lse, ws_d, ws_l2, rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (g_kv > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)g_kv), dim3(512), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g_kv), dim3(512), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dk,
                        (uint16_t*)dv, s.Hq, s.Hkv, s.Nq, s.Nk, nkt, scale, scale * kLog2e);
@@ -422,7 +461,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
     if (e != hipSuccess) return e;
   }
   if (g_dq > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL>), dim3((unsigned)g_dq), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g_dq), dim3(256), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dq, s.Hq,
                        s.Hkv, s.Nq, s.Nk, nqt, scale, scale * kLog2e);
@@ -437,8 +476,11 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            float* ws_d, const AttnShape& s, float scale, bool causal,
                            hipStream_t stream) {
-  return causal ? launch<true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream)
-                : launch<false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream);
+  if (s.d == 128)
+    return causal ? launch<128, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream)
+                  : launch<128, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream);
+  return causal ? launch<64, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream)
+                : launch<64, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream);
 }
 
 }  // namespace fa

@@ -32,7 +32,7 @@ hipError_t launch_decode_splitkv(const void* q, const void* k, const void* v, vo
                                  const void* bias, int bias_b, int bias_h, const AttnShape& s,
                                  float scale, bool causal, int n_splits, hipStream_t stream);
 
-// Backward (bwd_bf16.hip), head dim 128: D = rowsum(dout * out) into ws_d (fp32 [B, Hq, Nq]),
+// Backward (bwd_bf16.hip), head dim 64 or 128: D = rowsum(dout * out) into ws_d (fp32 [B, Hq, Nq]),
 // then dk/dv and dq; lse is the forward's natural-log logsumexp.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* out,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -234,7 +234,7 @@ def _bwd(lib, ws=A16, ws_bytes=1 << 40, lse=A16, dout=A16, dq=A16, dk=A16, dv=A1
 def test_backward_validation(lib):
     assert lib.attn_bwd_workspace_bytes(2, 16, 2048) == 2 * 16 * 2048 * 8
     assert lib.attn_bwd_workspace_bytes(-1, 16, 2048) == 0
-    assert _bwd(lib, d=64) == C["ATTN_ERR_HEADDIM"]  # head dim 128 only
+    assert _bwd(lib, d=96) == C["ATTN_ERR_HEADDIM"]  # head dim 64 or 128
     assert _bwd(lib, B=-1) == C["ATTN_ERR_SHAPE"]
     assert _bwd(lib, Hq=3) == C["ATTN_ERR_GQA"]
     assert _bwd(lib, scale=float("nan")) == C["ATTN_ERR_SCALE"]

@@ -78,6 +78,14 @@ CASES = [
     (1, 8, 2, 64, 512, False),
     (2, 8, 8, 384, 384, True),
 ]
+# head dimension 64: the same kinds of shapes
+CASES64 = [
+    (1, 2, 2, 128, 128, True),
+    (2, 4, 2, 200, 333, True),
+    (1, 4, 1, 257, 130, False),
+    (2, 2, 2, 77, 1, True),
+    (1, 8, 4, 300, 300, True),
+]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_Nq{}_Nk{}_{}".format(
@@ -85,6 +93,15 @@ CASES = [
 def test_backward_matches_oracle(case):
     B, Hq, Hkv, Nq, Nk, causal = case
     got, ref, _ = _run(B, Hq, Hkv, Nq, Nk, causal, seed=4000 + Nq + 3 * Nk)
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        _check(name, a, r)
+
+
+@pytest.mark.parametrize("case", CASES64, ids=lambda c: "d64_B{}_Hq{}_Hkv{}_Nq{}_Nk{}_{}".format(
+    *c[:5], "causal" if c[5] else "full"))
+def test_backward_head_dim_64(case):
+    B, Hq, Hkv, Nq, Nk, causal = case
+    got, ref, _ = _run(B, Hq, Hkv, Nq, Nk, causal, seed=4500 + Nq + 3 * Nk, d=64)
     for name, a, r in zip(("dq", "dk", "dv"), got, ref):
         _check(name, a, r)
 
@@ -146,7 +163,7 @@ def test_backward_without_query_rows_zeroes_dk_dv():
 
 
 def test_backward_rejects_other_head_dims():
-    q = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 2, 8, 96), dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros((1, 2, 8), dtype=torch.float32, device="cuda")
     with pytest.raises(fa.AttentionError, match="head dimension"):
         fa.attn_bwd(q, q, q, q, lse, q)

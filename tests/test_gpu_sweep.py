@@ -32,7 +32,7 @@ def _shapes(seed, n, d_choices=(64, 128)):
 
 FWD = _shapes(9100, 24)
 DEC = _shapes(9200, 16)
-BWD = _shapes(9300, 12, d_choices=(128,))
+BWD = _shapes(9300, 12)
 
 
 def _ids(c):
