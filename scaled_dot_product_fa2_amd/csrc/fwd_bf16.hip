@@ -26,8 +26,10 @@
 //   * Software pipelining: in steady state a step exponentiates block t while issuing block
 //     t+1's QK products, instruction by instruction (scheduling fences keep the order), and then
 //     issues block t's PV products 16 keys at a time while the next 16 keys are exponentiated.
-//     The matrix cores therefore run while the transcendental and VALU work issues.  Blocks that
-//     need a mask (the causal diagonal, a ragged end) run an unpipelined step instead.
+//     The matrix cores therefore run while the transcendental and VALU work issues.  The PV part
+//     is issued at raised wave priority, so the SIMD's other wave, in its vector-heavy QK part,
+//     fills the gaps between these products.  Blocks that need a mask (the causal diagonal, a
+//     ragged end) run an unpipelined step instead.
 //   * K/V blocks go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane, no
 //     register staging).  K runs one block ahead of V: at the start of step t, K[t+1] and V[t]
 //     are in LDS and K[t+2], V[t+1] are requested, so two buffers each suffice; every buffer is
