@@ -167,3 +167,18 @@ def test_backward_rejects_other_head_dims():
     lse = torch.zeros((1, 2, 8), dtype=torch.float32, device="cuda")
     with pytest.raises(fa.AttentionError, match="head dimension"):
         fa.attn_bwd(q, q, q, q, lse, q)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_without_keys_zeroes_dq(d):
+    # Nk = 0: every row has no visible key (forward: out = 0, lse = -inf), so no gradient flows
+    say(f"backward Nk=0 d={d}")
+    x = I.draw_qkv(4600 + d, 2, 4, 2, 70, 0, d)
+    q, k, v = upload(x)
+    dout = I.to_device(I.draw_grad(4601 + d, (2, 4, 70, d)), "bf16")
+    out, lse = fa.attn_fwd(q, k, v, causal=True)
+    dq = torch.full_like(q, float("nan"))
+    fa.attn_bwd(q, k, v, out, lse, dout, causal=True, dq=dq)
+    torch.cuda.synchronize()
+    assert bool((lse == -float("inf")).all())
+    assert bool((dq.float() == 0).all())
