@@ -20,6 +20,9 @@
 //   * combine kernel: one wave per (batch, query head, row); the split metadata is read by all
 //     lanes at once and the partial rows are accumulated in a fixed split order, so the result
 //     is deterministic.
+//   * When the (batch, KV head) pairs are a multiple of 8 (the XCD count), every workgroup of
+//     one pair, in both kernels, runs on the same XCD, so the combine reads the partials that
+//     the split wrote from that XCD's L2 instead of from memory.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -79,18 +82,34 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ wsO, float* __restrict__ wsML,
     const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
-    int Hq, int Hkv, int Nq, int Nk_cap, int S, int L, int nrg, float scale, float scale_log2) {
+    int Hq, int Hkv, int Nq, int Nk_cap, int S, int L, int nrg, float scale, float scale_log2,
+    int xcd_pairs) {
   using C = DecCfg<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, l16 = lane & 15;  // 16-lane group, query column
-  int n = blockIdx.x;
-  const int s = n % S;
-  n /= S;
-  const int rg = n % nrg;
-  n /= nrg;
-  const int hkv = n % Hkv, b = n / Hkv;
+  // workgroup -> (batch, KV head, row group, split).  Workgroup n runs on XCD n mod 8; when the
+  // (batch, KV head) pairs are a multiple of 8, all workgroups of one pair go to one XCD (pair p
+  // to XCD p mod 8), so the combine kernel, which maps its rows the same way, reads the partials
+  // from that XCD's L2.  Otherwise the split index runs fastest.
+  int s, rg, hkv, b;
+  if (xcd_pairs) {
+    const int per = nrg * S, j = blockIdx.x >> 3;
+    const int pair = (j / per) * 8 + (blockIdx.x & 7), w = j % per;
+    rg = w / S;
+    s = w % S;
+    hkv = pair % Hkv;
+    b = pair / Hkv;
+  } else {
+    int n = blockIdx.x;
+    s = n % S;
+    n /= S;
+    rg = n % nrg;
+    n /= nrg;
+    hkv = n % Hkv;
+    b = n / Hkv;
+  }
   const int G = Hq / Hkv, R = G * Nq;
   // keys of this batch element: all Nk_cap rows of K/V, or the first seqlens[b] (clamped); the
   // split chunks are those of the capacity, clipped to it
@@ -338,12 +357,18 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
                                                            const float* __restrict__ wsML,
                                                            uint16_t* __restrict__ O,
                                                            float* __restrict__ LSE, int rows,
-                                                           int S) {
+                                                           int S, int xcd_pairs, int R) {
   constexpr int E = D / 64;  // head-dim elements per lane
   constexpr int CH = 16;     // partial rows in flight per lane
   typedef float vecE __attribute__((ext_vector_type(E)));
   const int lane = threadIdx.x;
-  const int row = blockIdx.x;
+  // the R rows of a (batch, KV head) pair are consecutive; with the split kernel's XCD mapping,
+  // pair p's rows run on XCD p mod 8 as well
+  int row = blockIdx.x;
+  if (xcd_pairs) {
+    const int j = row >> 3;
+    row = ((j / R) * 8 + (row & 7)) * R + j % R;
+  }
   if (row >= rows) return;
   const f32x2* ml = (const f32x2*)(wsML + (size_t)row * S * 2);
   const float* src = wsO + (size_t)row * S * D + lane * E;
@@ -404,15 +429,16 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, float*
   const long long blocks = (long long)sh.B * sh.Hkv * nrg * S;
   const long long rows = (long long)sh.B * sh.Hq * sh.Nq;
   if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int xcd_pairs = ((long long)sh.B * sh.Hkv) % 8 == 0 ? 1 : 0;
   hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, BIAS>), dim3((unsigned)blocks), dim3(C::NT),
                      0, stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws_o,
                      ws_ml, seqlens, (const uint16_t*)bias, bias_b, bias_h, sh.Hq, sh.Hkv, sh.Nq,
-                     sh.Nk, S, L, nrg, scale, scale * kLog2e);
+                     sh.Nk, S, L, nrg, scale, scale * kLog2e, xcd_pairs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)rows), dim3(64), 0,
                      stream, (const float*)ws_o, (const float*)ws_ml, (uint16_t*)out, lse,
-                     (int)rows, S);
+                     (int)rows, S, xcd_pairs, R);
   return hipGetLastError();
 }
 

@@ -83,7 +83,8 @@ def test_config_decode_gqa(name):
 
 # (B, Hq, Hkv, Nq, Nk, d, causal, n_splits): ragged split lengths, one key per split, more than
 # 32 query rows per KV head (two row groups), non-causal, Nq > Nk (rows and splits with no
-# visible key), head dim 64, GQA ratios 1, 4 and 8.
+# visible key), head dim 64, GQA ratios 1, 4 and 8; (batch, KV head) pair counts that are
+# multiples of 8 (the XCD-grouped mapping of both kernels) with two row groups and with ragged ones.
 EDGE_CASES = [
     (2, 8, 2, 1, 1000, 128, True, 3),
     (1, 4, 4, 1, 33, 64, True, 33),
@@ -93,6 +94,8 @@ EDGE_CASES = [
     (1, 2, 2, 3, 257, 64, True, 7),
     (1, 32, 8, 4, 8192, 128, True, 16),
     (1, 8, 8, 1, 70, 128, False, 70),
+    (2, 64, 4, 2, 300, 64, True, 5),
+    (4, 12, 4, 3, 200, 128, False, 6),
 ]
 
 
