@@ -8,13 +8,15 @@
 // rows so that the K/V it streams is read once for all of them.
 //
 // gfx950 mapping:
-//   * split kernel: one workgroup (4 waves) per (batch, KV head, row group of 16, split).  The
-//     16 "query" columns of the MFMA are the Hq/Hkv query heads x Nq rows that share the KV head,
-//     so every K/V byte of the split is read from HBM exactly once.  Each wave streams its own
-//     32-key blocks (block w, w+4, ...) with non-temporal 16-byte buffer loads whose range ends
-//     at the split (later keys read as zero), keeps two blocks in flight in registers, stages
-//     the current one in a wave-private LDS slice, and keeps its own running (m, l, Oᵀ); the 4
-//     waves are merged through LDS at the end into one locally normalised partial.
+//   * split kernel: one workgroup per (batch, KV head, row group of 16, split).  The 16 "query"
+//     columns of the MFMA are the Hq/Hkv query heads x Nq rows that share the KV head, so every
+//     K/V byte of the split is read from HBM exactly once.  A grid with at least one workgroup
+//     per SIMD uses one-wave workgroups (all resident at once, one wave per SIMD); smaller grids
+//     use four waves per workgroup.  Each wave streams its own 32-key blocks (block w, w+NW, ...)
+//     with non-temporal 16-byte buffer loads whose range ends at the split (later keys read as
+//     zero), keeps the next block in flight in registers, stages the current one in a
+//     wave-private LDS slice, and keeps its own running (m, l, Oᵀ); four waves are merged through
+//     LDS at the end into one locally normalised partial, a lone wave stores its own.
 //   * Products on v_mfma_f32_16x16x32_bf16: Sᵀ = K·Qᵀ, then Oᵀ += Vᵀ·Pᵀ with Pᵀ taken straight
 //     from the score registers and Vᵀ from the transposing LDS read.
 //   * combine kernel: one wave per (batch, query head, row); the split metadata is read by all
@@ -31,11 +33,13 @@
 namespace fa {
 namespace {
 
-template <int D>
+constexpr long long kSimdCount = 1024;  // MI355X: 256 CUs x 4 SIMDs
+
+template <int D, int NW_>
 struct DecCfg {
   static constexpr int KB = 32;               // keys per wave block
   static constexpr int QC = 16;               // query columns per workgroup (MFMA N)
-  static constexpr int NW = 4;                // waves per workgroup
+  static constexpr int NW = NW_;              // waves per workgroup (1 or 4)
   static constexpr int NT = 64 * NW;
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
   static constexpr int NCH = KB * CPR / 64;   // chunks per lane per tensor per block
@@ -77,14 +81,14 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x + __shfl_xor(x, 16);
 }
 
-template <int D, bool CAUSAL, bool BIAS>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(
+template <int D, bool CAUSAL, bool BIAS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ wsO, float* __restrict__ wsML,
     const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
     int Hq, int Hkv, int Nq, int Nk_cap, int S, int L, int nrg, float scale, float scale_log2,
     int xcd_pairs) {
-  using C = DecCfg<D>;
+  using C = DecCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -173,11 +177,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     }
   };
 
-  u32x4 kA[C::NCH], vA[C::NCH], kB[C::NCH], vB[C::NCH];
-  u32x2 bA[2], bB[2];
+  u32x4 kst[C::NCH], vst[C::NCH];
+  u32x2 bst[2];
   const int kb0 = wave;
-  if (kb0 < nkb) gload(kA, vA, bA, kb0);
-  if (kb0 + C::NW < nkb) gload(kB, vB, bB, kb0 + C::NW);
+  if (kb0 < nkb) gload(kst, vst, bst, kb0);
 
   // Qᵀ as the B operand of Sᵀ = K·Qᵀ (16x16x32): lane holds query column l16, head-dim slots
   // 32c + 8grp .. +7.
@@ -265,25 +268,42 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     }
   };
 
-  for (int kb = kb0; kb < nkb; kb += 2 * C::NW) {
-    swrite(kA, vA);
+  // one block in flight per wave: the next block's loads are issued once the current one is in
+  // LDS, and land while it is computed (measured: a second or third block in flight per wave
+  // was 1-9% slower, as more concurrent streams compete for the DRAM pages)
+  for (int kb = kb0; kb < nkb; kb += C::NW) {
+    swrite(kst, vst);
     wave_lds_sync();
-    const u32x2 bc[2] = {bA[0], bA[1]};
-    if (kb + 2 * C::NW < nkb) gload(kA, vA, bA, kb + 2 * C::NW);  // keeps two blocks in flight
+    const u32x2 bc[2] = {bst[0], bst[1]};
+    if (kb + C::NW < nkb) gload(kst, vst, bst, kb + C::NW);
     compute(kb, bc);
     wave_lds_sync();  // this block's LDS reads precede the next block's writes
-    if (kb + C::NW < nkb) {
-      swrite(kB, vB);
-      wave_lds_sync();
-      const u32x2 bd[2] = {bB[0], bB[1]};
-      if (kb + 3 * C::NW < nkb) gload(kB, vB, bB, kb + 3 * C::NW);
-      compute(kb + C::NW, bd);
-      wave_lds_sync();
-    }
   }
 
-  // merge the 4 waves' (m, l, Oᵀ) into one locally normalised partial for the split
   const float l_tot = quad_sum(l_run);
+  if constexpr (C::NW == 1) {
+    // the wave is the whole split: the exact max M of its keys and the sum against M give the
+    // metadata, and Oᵀ / l (both against the reference max) is the locally normalised partial,
+    // stored straight from the accumulator layout (lane (l16, grp), register i of tile db holds
+    // head-dim slot 16 db + 4 grp + i of query column l16)
+    if (row_ok) {
+      const float M = l_tot > 0.f ? m_true : -INFINITY;
+      const float ew = l_tot > 0.f ? fast_exp2((m_run - M) * scale_log2) : 0.f;
+      const float Lsum = ew * l_tot;
+      const float f = Lsum > 0.f ? ew * (1.f / Lsum) : 0.f;
+      const size_t slot = (((size_t)b * Hq + hq) * Nq + qi) * S + s;
+      float* dst = wsO + slot * D + 4 * grp;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) *(f32x4*)(dst + 16 * db) = oacc[db] * f;
+      if (grp == 0) {
+        wsML[slot * 2 + 0] = Lsum > 0.f ? M * scale : -INFINITY;
+        wsML[slot * 2 + 1] = Lsum;
+      }
+    }
+    return;
+  }
+
+  // merge the waves' (m, l, Oᵀ) into one locally normalised partial for the split
   __syncthreads();
   float* ocb = (float*)smem;                 // [NW][QC][OROW] unnormalised Oᵀ rows
   float* mlb = ocb + C::NW * C::QC * C::OROW;  // [NW][QC][3]: exact max, reference max, sum
@@ -422,18 +442,30 @@ template <int D, bool CAUSAL, bool BIAS>
 hipError_t launch(const void* q, const void* k, const void* v, void* out, float* lse,
                   float* ws_o, float* ws_ml, const int* seqlens, const void* bias, int bias_b,
                   int bias_h, const AttnShape& sh, float scale, int S, hipStream_t stream) {
-  using C = DecCfg<D>;
+  constexpr int QC = DecCfg<D, 1>::QC;
   const int L = (sh.Nk + S - 1) / S;
   const int R = (sh.Hq / sh.Hkv) * sh.Nq;
-  const int nrg = (R + C::QC - 1) / C::QC;
+  const int nrg = (R + QC - 1) / QC;
   const long long blocks = (long long)sh.B * sh.Hkv * nrg * S;
   const long long rows = (long long)sh.B * sh.Hq * sh.Nq;
   if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int xcd_pairs = ((long long)sh.B * sh.Hkv) % 8 == 0 ? 1 : 0;
-  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, BIAS>), dim3((unsigned)blocks), dim3(C::NT),
-                     0, stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, ws_o,
-                     ws_ml, seqlens, (const uint16_t*)bias, bias_b, bias_h, sh.Hq, sh.Hkv, sh.Nq,
-                     sh.Nk, S, L, nrg, scale, scale * kLog2e, xcd_pairs);
+  // A grid with a workgroup for every SIMD (256 CUs x 4) runs one wave per split, all resident
+  // at once; smaller grids split each split over four waves so that the chip still fills.
+  // Measured on the GQA decode workloads (1024 workgroups): one-wave splits 46.2 / 48.5 us
+  // (Nq = 1 / 4) against 45.6 / 50.7 us with four-wave splits in two rounds.
+  if (blocks >= kSimdCount)
+    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, BIAS, 1>), dim3((unsigned)blocks),
+                       dim3(64), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
+                       (const uint16_t*)v, ws_o, ws_ml, seqlens, (const uint16_t*)bias, bias_b,
+                       bias_h, sh.Hq, sh.Hkv, sh.Nq, sh.Nk, S, L, nrg, scale, scale * kLog2e,
+                       xcd_pairs);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, BIAS, 4>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
+                       (const uint16_t*)v, ws_o, ws_ml, seqlens, (const uint16_t*)bias, bias_b,
+                       bias_h, sh.Hq, sh.Hkv, sh.Nq, sh.Nk, S, L, nrg, scale, scale * kLog2e,
+                       xcd_pairs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)rows), dim3(64), 0,
