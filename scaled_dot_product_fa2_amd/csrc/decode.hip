@@ -11,12 +11,13 @@
 //   * split kernel: one workgroup per (batch, KV head, row group of 16, split).  The 16 "query"
 //     columns of the MFMA are the Hq/Hkv query heads x Nq rows that share the KV head, so every
 //     K/V byte of the split is read from HBM exactly once.  A grid with at least one workgroup
-//     per SIMD uses one-wave workgroups (all resident at once, one wave per SIMD); smaller grids
-//     use four waves per workgroup.  Each wave streams its own 32-key blocks (block w, w+NW, ...)
-//     with non-temporal 16-byte buffer loads whose range ends at the split (later keys read as
-//     zero), keeps the next block in flight in registers, stages the current one in a
-//     wave-private LDS slice, and keeps its own running (m, l, Oᵀ); four waves are merged through
-//     LDS at the end into one locally normalised partial, a lone wave stores its own.
+//     per SIMD and row groups at least half full uses one-wave workgroups (all resident at once,
+//     one wave per SIMD); other grids use four waves per workgroup.  Each wave streams its own
+//     32-key blocks (block w, w+NW, ...) with non-temporal 16-byte buffer loads whose range ends
+//     at the split (later keys read as zero), keeps the next block (four waves) or two (a lone
+//     wave) in flight in registers, stages the current one in a wave-private LDS slice, and keeps
+//     its own running (m, l, Oᵀ); four waves are merged through LDS at the end into one locally
+//     normalised partial, a lone wave stores its own.
 //   * Products on v_mfma_f32_16x16x32_bf16: Sᵀ = K·Qᵀ, then Oᵀ += Vᵀ·Pᵀ with Pᵀ taken straight
 //     from the score registers and Vᵀ from the transposing LDS read.
 //   * combine kernel: one wave per (batch, query head, row); the split metadata is read by all
@@ -177,10 +178,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_split_kernel(
     }
   };
 
-  u32x4 kst[C::NCH], vst[C::NCH];
-  u32x2 bst[2];
+  // blocks in flight per wave: two for a lone wave, one for each of four (a second or third one
+  // there measured 1-9% slower, as more concurrent streams compete for the DRAM pages)
+  constexpr int NB = C::NW == 1 ? 2 : 1;
+  u32x4 kst[NB][C::NCH], vst[NB][C::NCH];
+  u32x2 bst[NB][2];
   const int kb0 = wave;
-  if (kb0 < nkb) gload(kst, vst, bst, kb0);
+#pragma unroll
+  for (int u = 0; u < NB; ++u)
+    if (kb0 + u * C::NW < nkb) gload(kst[u], vst[u], bst[u], kb0 + u * C::NW);
 
   // Qᵀ as the B operand of Sᵀ = K·Qᵀ (16x16x32): lane holds query column l16, head-dim slots
   // 32c + 8grp .. +7.
@@ -268,16 +274,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_split_kernel(
     }
   };
 
-  // one block in flight per wave: the next block's loads are issued once the current one is in
-  // LDS, and land while it is computed (measured: a second or third block in flight per wave
-  // was 1-9% slower, as more concurrent streams compete for the DRAM pages)
-  for (int kb = kb0; kb < nkb; kb += C::NW) {
-    swrite(kst, vst);
-    wave_lds_sync();
-    const u32x2 bc[2] = {bst[0], bst[1]};
-    if (kb + C::NW < nkb) gload(kst, vst, bst, kb + C::NW);
-    compute(kb, bc);
-    wave_lds_sync();  // this block's LDS reads precede the next block's writes
+  // a block's registers are refilled with the block NB further on as soon as it is in LDS, so
+  // the loads land while this block and the next NB - 1 are computed
+  for (int kb = kb0; kb < nkb; kb += NB * C::NW) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int kbu = kb + u * C::NW;
+      if (kbu < nkb) {
+        swrite(kst[u], vst[u]);
+        wave_lds_sync();
+        const u32x2 bc[2] = {bst[u][0], bst[u][1]};
+        if (kbu + NB * C::NW < nkb) gload(kst[u], vst[u], bst[u], kbu + NB * C::NW);
+        compute(kbu, bc);
+        wave_lds_sync();  // this block's LDS reads precede the next block's writes
+      }
+    }
   }
 
   const float l_tot = quad_sum(l_run);
@@ -450,11 +461,13 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, float*
   const long long rows = (long long)sh.B * sh.Hq * sh.Nq;
   if (blocks > 0x7fffffffLL || rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int xcd_pairs = ((long long)sh.B * sh.Hkv) % 8 == 0 ? 1 : 0;
-  // A grid with a workgroup for every SIMD (256 CUs x 4) runs one wave per split, all resident
-  // at once; smaller grids split each split over four waves so that the chip still fills.
-  // Measured on the GQA decode workloads (1024 workgroups): one-wave splits 46.2 / 48.5 us
-  // (Nq = 1 / 4) against 45.6 / 50.7 us with four-wave splits in two rounds.
-  if (blocks >= kSimdCount)
+  // One wave per split when the grid has a workgroup for every SIMD (256 CUs x 4, all resident
+  // at once) and at least half of a row group's 16 query columns are in use; otherwise four
+  // waves per split, whose LDS merge is cheap with few columns and which fill the chip on small
+  // grids.  Measured on the GQA decode workloads (1024 workgroups, four-wave vs one-wave):
+  // Nq = 4 (16 columns) 49.4-50.0 vs 47.9-48.0 us, with a bias 53.0 vs 51.0; Nq = 1 (4 columns)
+  // 45.4 vs 46.2, with a bias 47.9 vs 49.6.
+  if (blocks >= kSimdCount && min(R, QC) >= QC / 2)
     hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, BIAS, 1>), dim3((unsigned)blocks),
                        dim3(64), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, ws_o, ws_ml, seqlens, (const uint16_t*)bias, bias_b,

@@ -85,9 +85,9 @@ def test_config_decode_gqa(name):
 # 32 query rows per KV head (two row groups), non-causal, Nq > Nk (rows and splits with no
 # visible key), head dim 64, GQA ratios 1, 4 and 8; (batch, KV head) pair counts that are
 # multiples of 8 (the XCD-grouped mapping of both kernels) with two row groups and with ragged ones;
-# grids of 1024 workgroups or more (one wave per split): head dim 64 with ragged splits, 9 pairs
-# (not a multiple of 8) with two row groups in two rounds of workgroups, and splits past the end
-# of the keys (L = 5, so the last splits are empty).
+# grids of 1024 workgroups or more with at least 8 query rows per KV head (one wave per split):
+# head dim 64 with ragged splits, 9 pairs (not a multiple of 8) with two row groups in two rounds
+# of workgroups, and splits past the end of the keys (L = 5, so the last splits are empty).
 EDGE_CASES = [
     (2, 8, 2, 1, 1000, 128, True, 3),
     (1, 4, 4, 1, 33, 64, True, 33),
@@ -99,7 +99,7 @@ EDGE_CASES = [
     (1, 8, 8, 1, 70, 128, False, 70),
     (2, 64, 4, 2, 300, 64, True, 5),
     (4, 12, 4, 3, 200, 128, False, 6),
-    (4, 8, 4, 3, 3000, 64, True, 64),
+    (4, 8, 4, 4, 3000, 64, True, 64),
     (3, 12, 3, 5, 2000, 128, False, 128),
     (2, 16, 2, 1, 1030, 128, True, 257),
 ]
