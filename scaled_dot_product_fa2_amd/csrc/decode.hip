@@ -83,7 +83,7 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 template <int D, bool CAUSAL, bool BIAS, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_split_kernel(
+__global__ __launch_bounds__(64 * NW, NW == 1 ? 1 : 2) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ wsO, float* __restrict__ wsML,
     const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
