@@ -87,7 +87,8 @@ def test_config_decode_gqa(name):
 # multiples of 8 (the XCD-grouped mapping of both kernels) with two row groups and with ragged ones;
 # grids of 1024 workgroups or more with at least 8 query rows per KV head (one wave per split):
 # head dim 64 with ragged splits, 9 pairs (not a multiple of 8) with two row groups in two rounds
-# of workgroups, and splits past the end of the keys (L = 5, so the last splits are empty).
+# of workgroups, splits past the end of the keys (L = 5, so the last splits are empty), and more
+# query rows than keys (row 0 sees no key).
 EDGE_CASES = [
     (2, 8, 2, 1, 1000, 128, True, 3),
     (1, 4, 4, 1, 33, 64, True, 33),
@@ -102,6 +103,7 @@ EDGE_CASES = [
     (4, 8, 4, 4, 3000, 64, True, 64),
     (3, 12, 3, 5, 2000, 128, False, 128),
     (2, 16, 2, 1, 1030, 128, True, 257),
+    (128, 8, 4, 4, 3, 64, True, 3),
 ]
 
 
@@ -142,6 +144,23 @@ def test_deterministic_and_workspace_reuse():
     assert not bool(torch.isnan(out.float()).any()) and not bool(torch.isnan(lse).any())
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
+@pytest.mark.parametrize("B", [2, 256], ids=["four_wave", "one_wave"])
+def test_decode_without_keys(B):
+    # Nk = 0 (one split): no row sees a key, so O = 0, LSE = -inf and the split's metadata is
+    # (-inf, 0); B = 256 gives 1024 split workgroups of 8 rows each (one wave per split)
+    Hq, Hkv, Nq, d = 8, 4, 4, 128
+    say(f"decode Nk=0 B={B}")
+    q = I.to_device(I.draw_qkv(4700 + B, B, Hq, Hkv, Nq, 1, d).q, "bf16")
+    k = torch.empty((B, Hkv, 0, d), dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, Hq, Nq), float("nan"), device="cuda")
+    out, lse, ws = fa.attn_decode_splitkv(q, k, k, 1, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((out.float() == 0).all()) and bool((lse == -float("inf")).all())
+    O_s, m_s, l_s = _workspace(ws, B, Hq, Nq, 1, d)
+    assert np.all(O_s == 0) and np.all(np.isneginf(m_s)) and np.all(l_s == 0)
 
 
 def test_invalid_decode_arguments():
