@@ -354,10 +354,13 @@ def _accumulate(acc: np.ndarray, x: np.ndarray) -> np.ndarray:
     return acc + x
 
 
-def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool):
+def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool, seqlens_k=None):
     """(dq [B,Hq,Nq,d], dk [B,Hkv,Nk,d], dv [B,Hkv,Nk,d]): the gradients of L = Σ dout ∘ O for
     O = softmax(scale·q·kᵀ + causal mask)·v, in fp64, from the definition (see the module
-    docstring).  Small and medium inputs only: every (batch, head) keeps its [Nq, Nk] matrices."""
+    docstring).  With ``seqlens_k`` (the reading of ``attention_fp64``) element b has only its
+    first seqlens_k[b] keys: the causal mask is aligned to the end of those, and the keys past
+    them, which do not take part in O, get zero gradients.  Small and medium inputs only: every
+    (batch, head) keeps its [Nq, Nk] matrices."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -366,19 +369,23 @@ def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool):
     if dout.shape != q.shape:
         raise ValueError(f"dout must have the shape of q {q.shape}, got {dout.shape}")
     scale = _resolve_scale(scale, d)
+    L = _key_lengths(seqlens_k, B, Nk)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     rows = np.arange(Nq)
-    vis = visible_mask(rows, Nq, Nk, causal)
     for b in range(B):
+        Lb = int(L[b])
+        if Lb == 0:
+            continue  # no key: O = 0 whatever the inputs, every gradient is zero
+        vis = visible_mask(rows, Nq, Lb, causal)
         for hq in range(Hq):
             hkv = _kv_head(hq, Hq, Hkv)
-            kh, vh, qh, doh = k[b, hkv], v[b, hkv], q[b, hq], dout[b, hq]
+            kh, vh, qh, doh = k[b, hkv, :Lb], v[b, hkv, :Lb], q[b, hq], dout[b, hq]
             p, _, _ = _masked_softmax(_scores(qh, kh, scale), vis)
             dp = doh @ vh.T
             ds = _softmax_backward(p, dp)
             dq[b, hq] = scale * (ds @ kh)
-            dk[b, hkv] = _accumulate(dk[b, hkv], scale * (ds.T @ qh))
-            dv[b, hkv] = _accumulate(dv[b, hkv], p.T @ doh)
+            dk[b, hkv, :Lb] = _accumulate(dk[b, hkv, :Lb], scale * (ds.T @ qh))
+            dv[b, hkv, :Lb] = _accumulate(dv[b, hkv, :Lb], p.T @ doh)
     return dq, dk, dv

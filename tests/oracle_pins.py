@@ -522,6 +522,38 @@ def pin_bwd_finite_differences():
             _close(gx, num, 1e-7, f"finite differences causal={causal} tensor {'qkv'[t]}")
 
 
+def pin_bwd_varlen_finite_differences():
+    """With per-element key lengths (0, 1, a ragged 3 and all 5 keys), every gradient element
+    against a central difference of L = Σ g ∘ O through the forward oracle with those lengths
+    (pinned above): keys past an element's length do not move O, so their gradients are zero,
+    and the causal mask follows the length."""
+    h = 1e-6
+    L = [0, 1, 3, 5]
+    for causal, Nq in ((False, 4), (True, 4), (True, 2)):
+        B, Hq, Hkv, Nk, d = 4, 2, 1, 5, 3
+        q, k, v = _rand(730, B, Hq, Nq, d), _rand(731, B, Hkv, Nk, d), _rand(732, B, Hkv, Nk, d)
+        g = _rand(733, B, Hq, Nq, d)
+
+        def loss(q_, k_, v_):
+            O, _ = A.attention_fp64(q_, k_, v_, 0.6, causal, seqlens_k=L)
+            return float((O * g).sum())
+
+        grads = A.attention_backward_fp64(q, k, v, g, 0.6, causal, seqlens_k=L)
+        for t, (x, gx) in enumerate(zip((q, k, v), grads)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p, args_m = [q, k, v], [q, k, v]
+                args_p[t], args_m[t] = xp, xm
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(gx, num, 1e-7, f"varlen finite differences causal={causal} tensor {'qkv'[t]}")
+        for b, Lb in enumerate(L):
+            assert np.all(grads[1][b, :, Lb:] == 0) and np.all(grads[2][b, :, Lb:] == 0)
+        assert np.all(grads[0][0] == 0), "no key: dq = 0"
+
+
 def pin_bwd_shift_invariances():
     """Shifting every key by c leaves O unchanged (a row-constant score change), so Σ_j dK_j = 0;
     shifting every value by c shifts O by c on rows with a visible key, so Σ_j dV_j = Σ dO over
@@ -584,6 +616,7 @@ ALL_PINS = [
     pin_bias_rank_one_is_extra_head_dim,
     pin_bias_neg_inf_is_mask,
     pin_bwd_finite_differences,
+    pin_bwd_varlen_finite_differences,
     pin_bwd_shift_invariances,
     pin_bwd_gqa_equals_repeated_heads,
 ]
