@@ -224,6 +224,21 @@ SDPA_FA2_API int attn_bwd(const void* q, const void* k, const void* v, const voi
              int B, int Hq, int Hkv, int Nq, int Nk, int d,
              float scale, int causal, void* stream);
 
+/*
+ * attn_bwd_ex -- attn_bwd for a forward that took per-batch key lengths (attn_fwd_ex with
+ * seqlens_k and no bias).  seqlens_k has the meaning and checks of the extras above (device
+ * int32 [B], 4-byte aligned, values clamped to [0, Nk]; NULL makes the call attn_bwd): element b
+ * has only its first seqlens_k[b] keys, with the causal mask aligned to their end, and the K/V
+ * rows past them, which take no part in the forward, get dk = dv = 0 (every row of dk and dv up
+ * to Nk is written).  A forward with a bias has no backward here.  Other arguments and errors as
+ * for attn_bwd; out and lse must come from the forward with the same lengths.
+ */
+SDPA_FA2_API int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out,
+                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes, const int* seqlens_k,
+                int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                float scale, int causal, void* stream);
+
 /* attn_status_string -- a static, NUL-terminated description of a status code. */
 SDPA_FA2_API const char* attn_status_string(int status);
 

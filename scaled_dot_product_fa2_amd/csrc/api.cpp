@@ -214,6 +214,14 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              const void* dout, void* dq, void* dk, void* dv, void* workspace,
              size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
              int causal, void* stream) {
+  return attn_bwd_ex(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, nullptr, B,
+                     Hq, Hkv, Nq, Nk, d, scale, causal, stream);
+}
+
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, const int* seqlens_k, int B, int Hq, int Hkv, int Nq,
+                int Nk, int d, float scale, int causal, void* stream) {
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d < 0) return ATTN_ERR_SHAPE;
   if (Nq >= kMaxSeq || Nk >= kMaxSeq) return ATTN_ERR_SHAPE;
   uint64_t tmp;
@@ -237,6 +245,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
     return ATTN_ERR_ALIGN;
   if (has_k && (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16)))
     return ATTN_ERR_ALIGN;
+  if (seqlens_k != nullptr && !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGN;
   if (has_q) {
     const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
     if (need == 0 || workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
@@ -248,7 +257,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
     return ATTN_ERR_SHAPE;
   const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
   return launch_status(fa::launch_bwd_bf16(q, k, v, out, lse, dout, dq, dk, dv, (float*)workspace,
-                                           s, resolve_scale(scale, d), causal != 0,
+                                           seqlens_k, s, resolve_scale(scale, d), causal != 0,
                                            (hipStream_t)stream));
 }
 

@@ -173,7 +173,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dQ,
-    int Hq, int Hkv, int Nq, int Nk, int nqt, float scale, float scale_log2) {
+    const int* __restrict__ seqlens, int Hq, int Hkv, int Nq, int Nk_cap, int nqt, float scale,
+    float scale_log2) {
   constexpr int TILE = Geo<D>::TILE, NCB = Geo<D>::NCB, NDB = Geo<D>::NDB;
   __shared__ __attribute__((aligned(1024))) uint16_t kl0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t kl1[TILE];
@@ -186,10 +187,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int BH = gridDim.x / nqt;
   const int bh = blockIdx.x % BH, qt = nqt - 1 - blockIdx.x / BH;  // heaviest blocks first
   const int b = bh / Hq, hq = bh - b * Hq, hkv = hq / (Hq / Hkv);
+  // keys of this batch element: all Nk_cap rows of K/V, or the first seqlens[b] (clamped)
+  const int Nk = seqlens ? min(max(seqlens[b], 0), Nk_cap) : Nk_cap;
   const int off = Nk - Nq;
   const int qw0 = qt * 128 + wave * 32, my_q = qw0 + l32;
-  const uint16_t* kg = K + (size_t)(b * Hkv + hkv) * Nk * D;
-  const uint16_t* vg = V + (size_t)(b * Hkv + hkv) * Nk * D;
+  const uint16_t* kg = K + (size_t)(b * Hkv + hkv) * Nk_cap * D;
+  const uint16_t* vg = V + (size_t)(b * Hkv + hkv) * Nk_cap * D;
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(Nq - 1, qt * 128 + 127) + off + 1);
@@ -285,8 +288,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int Hq, int Hkv, int Nq, int Nk, int nkt, float scale,
-    float scale_log2) {
+    uint16_t* __restrict__ dV, const int* __restrict__ seqlens, int Hq, int Hkv, int Nq,
+    int Nk_cap, int nkt, float scale, float scale_log2) {
   constexpr int TILE = Geo<D>::TILE, NCB = Geo<D>::NCB, NDB = Geo<D>::NDB;
   __shared__ __attribute__((aligned(1024))) uint16_t qls[3][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gls[3][TILE];
@@ -303,6 +306,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int BHk = gridDim.x / nkt;
   const int bhk = blockIdx.x % BHk, kt = blockIdx.x / BHk;
   const int b = bhk / Hkv, hkv = bhk - b * Hkv, G = Hq / Hkv;
+  // keys of this batch element (as in the dQ kernel); keys past them keep zero gradients
+  const int Nk = seqlens ? min(max(seqlens[b], 0), Nk_cap) : Nk_cap;
   const int off = Nk - Nq;
   const int kw0 = kt * 128 + pair * 32, my_k = kw0 + l32;
 
@@ -310,7 +315,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   u32x4 bf[NCB];
   {
     const bool ok = my_k < Nk;
-    const uint16_t* row = (do_k ? V : K) + ((size_t)bhk * Nk + min(my_k, Nk - 1)) * D;
+    const uint16_t* row =
+        (do_k ? V : K) + ((size_t)bhk * Nk_cap + min(my_k, max(Nk - 1, 0))) * D;
 #pragma unroll
     for (int c = 0; c < NCB; ++c)
       bf[c] = ok ? *(const u32x4*)(row + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int q_first = CAUSAL ? max(0, kt * 128 - off) : 0;
   const int qb0 = q_first / BT, nqb = (Nq + BT - 1) / BT;
   const int per_head = max(0, nqb - qb0);
-  const int n_steps = G * per_head;
+  const int n_steps = kt * 128 < Nk ? G * per_head : 0;  // no key of this tile exists: zeros
 
   auto stage = [&](int step, int buf) {
     const int g = step / per_head, qb = qb0 + step - g * per_head;
@@ -429,14 +435,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         acc[db] = mfma32x32x16(read_tr<D>(at, tl.tr_base, 16 * g, db), pb[g], acc[db]);
     __builtin_amdgcn_s_setprio(0);
   }
-  if (my_k < Nk)
-    store_rowT<D>((do_k ? dK : dV) + ((size_t)bhk * Nk + my_k) * D, acc, do_k ? scale : 1.f, h);
+  if (my_k < Nk_cap)
+    store_rowT<D>((do_k ? dK : dV) + ((size_t)bhk * Nk_cap + my_k) * D, acc, do_k ? scale : 1.f,
+                  h);
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, const void* out, const float* lse,
-                  const void* dout, void* dq, void* dk, void* dv, float* ws_d, const AttnShape& s,
-                  float scale, hipStream_t stream) {
+                  const void* dout, void* dq, void* dk, void* dv, float* ws_d, const int* seqlens,
+                  const AttnShape& s, float scale, hipStream_t stream) {
   const long long rows = (long long)s.B * s.Hq * s.Nq;
   float* const ws_l2 = ws_d + rows;  // the workspace holds D, then the log2-unit references
   const int nqt = (s.Nq + 127) / 128, nkt = (s.Nk + 127) / 128;
@@ -456,15 +463,16 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g_kv), dim3(512), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dk,
-                       (uint16_t*)dv, s.Hq, s.Hkv, s.Nq, s.Nk, nkt, scale, scale * kLog2e);
+                       (uint16_t*)dv, seqlens, s.Hq, s.Hkv, s.Nq, s.Nk, nkt, scale,
+                       scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (g_dq > 0) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g_dq), dim3(256), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dq, s.Hq,
-                       s.Hkv, s.Nq, s.Nk, nqt, scale, scale * kLog2e);
+                       (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dq,
+                       seqlens, s.Hq, s.Hkv, s.Nq, s.Nk, nqt, scale, scale * kLog2e);
     e = hipGetLastError();
   }
   return e;
@@ -474,13 +482,17 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* out,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* ws_d, const AttnShape& s, float scale, bool causal,
-                           hipStream_t stream) {
+                           float* ws_d, const int* seqlens, const AttnShape& s, float scale,
+                           bool causal, hipStream_t stream) {
   if (s.d == 128)
-    return causal ? launch<128, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream)
-                  : launch<128, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream);
-  return causal ? launch<64, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream)
-                : launch<64, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, s, scale, stream);
+    return causal ? launch<128, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, s, scale,
+                                      stream)
+                  : launch<128, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, s,
+                                       scale, stream);
+  return causal ? launch<64, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, s, scale,
+                                   stream)
+                : launch<64, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, s, scale,
+                                    stream);
 }
 
 }  // namespace fa

@@ -33,10 +33,11 @@ hipError_t launch_decode_splitkv(const void* q, const void* k, const void* v, vo
                                  float scale, bool causal, int n_splits, hipStream_t stream);
 
 // Backward (bwd_bf16.hip), head dim 64 or 128: D = rowsum(dout * out) into ws_d (fp32 [B, Hq, Nq]),
-// then dk/dv and dq; lse is the forward's natural-log logsumexp.
+// then dk/dv and dq; lse is the forward's natural-log logsumexp.  seqlens (device int32 [B], or
+// nullptr) limits batch element b to its first seqlens[b] keys, as in the forward.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* out,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* ws_d, const AttnShape& s, float scale, bool causal,
-                           hipStream_t stream);
+                           float* ws_d, const int* seqlens, const AttnShape& s, float scale,
+                           bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -251,3 +251,17 @@ def test_backward_validation(lib):
     # no query rows: the query-side pointers and the workspace are not needed (dk, dv are)
     assert _bwd(lib, Nq=0, q=None, o=None, lse=None, dout=None, dq=None, ws=None, k=None) == \
         C["ATTN_ERR_NULL"]
+
+
+def test_backward_with_lengths_validation(lib):
+    # attn_bwd_ex checks what attn_bwd checks, plus the alignment of the length array
+    def bwd_ex(seqlens, **kw):
+        a = {**GOOD, **kw}
+        return lib.attn_bwd_ex(A16, A16, A16, A16, A16, A16, A16, A16, A16, A16, 1 << 40, seqlens,
+                               a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                               a["causal"], None)
+
+    assert bwd_ex(A16 + 2) == C["ATTN_ERR_ALIGN"]
+    assert bwd_ex(A16, d=96) == C["ATTN_ERR_HEADDIM"]
+    assert bwd_ex(A16, Hq=3) == C["ATTN_ERR_GQA"]
+    assert bwd_ex(None, B=0) == C["ATTN_OK"]

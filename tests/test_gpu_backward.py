@@ -182,3 +182,64 @@ def test_backward_without_keys_zeroes_dq(d):
     torch.cuda.synchronize()
     assert bool((lse == -float("inf")).all())
     assert bool((dq.float() == 0).all())
+
+
+# per-batch key lengths (attn_bwd_ex): (B, Hq, Hkv, Nq, Nk capacity, d, causal, lengths) with
+# lengths 0, 1, ragged, whole 128-key tiles and the capacity; Nq above a length (rows without a
+# key); GQA; head dims 128 and 64
+VARLEN = [
+    (4, 4, 2, 130, 300, 128, True, [0, 1, 257, 300]),
+    (3, 2, 1, 200, 200, 64, False, [64, 199, 128]),
+    (2, 8, 2, 64, 520, 128, True, [520, 130]),
+    (4, 2, 2, 300, 130, 128, True, [130, 0, 77, 128]),
+    (2, 8, 2, 150, 333, 64, True, [333, 200]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "B{}_Hq{}_Hkv{}_Nq{}_cap{}_d{}_{}".format(
+    *c[:6], "causal" if c[6] else "full"))
+def test_backward_with_key_lengths(case):
+    B, Hq, Hkv, Nq, Nk, d, causal, L = case
+    seed = 4800 + Nq + 7 * Nk + d
+    x = I.draw_qkv(seed, B, Hq, Hkv, Nq, Nk, d)
+    g_bits = I.draw_grad(seed + 1, (B, Hq, Nq, d))
+    q, k, v = upload(x)
+    dout = I.to_device(g_bits, "bf16")
+    lens = torch.as_tensor(np.asarray(L, np.int32), device="cuda")
+    s32 = _s32(d)
+    say(f"backward with lengths {case}")
+    out, lse = fa.attn_fwd_ex(q, k, v, causal=causal, scale=s32, seqlens_k=lens)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    fa.attn_bwd(q, k, v, out, lse, dout, causal=causal, scale=s32, dq=dq, dk=dk, dv=dv,
+                seqlens_k=lens)
+    torch.cuda.synchronize()
+    g = I.bf16_bits_to_f32(g_bits).astype(np.float64)
+    ref = A.attention_backward_fp64(*x.as_f64(), g, s32, causal, seqlens_k=L)
+    got = [to_f64(t) for t in (dq, dk, dv)]
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        _check(name, a, r)
+    for b, Lb in enumerate(L):  # rows of K/V past the length: exactly zero, and written
+        assert np.all(got[1][b, :, Lb:] == 0) and np.all(got[2][b, :, Lb:] == 0), f"b={b}"
+        if Lb == 0:
+            assert np.all(got[0][b] == 0), f"b={b}: no key, dq must be 0"
+
+
+def test_backward_with_lengths_matches_truncated_tensors():
+    # one element, 333 of 520 keys: bit-identical to the plain backward on K/V cut to 333 keys
+    B, Hq, Hkv, Nq, Nk, Lb, d = 1, 4, 2, 200, 520, 333, 128
+    x = I.draw_qkv(4900, B, Hq, Hkv, Nq, Nk, d)
+    q, k, v = upload(x)
+    dout = I.to_device(I.draw_grad(4901, (B, Hq, Nq, d)), "bf16")
+    lens = torch.full((1,), Lb, dtype=torch.int32, device="cuda")
+    say("backward with lengths vs truncated K/V")
+    out, lse = fa.attn_fwd_ex(q, k, v, causal=True, seqlens_k=lens)
+    dq, dk, dv = fa.attn_bwd(q, k, v, out, lse, dout, causal=True, seqlens_k=lens)
+    kt, vt = k[:, :, :Lb].contiguous(), v[:, :, :Lb].contiguous()
+    out_t, lse_t = fa.attn_fwd(q, kt, vt, causal=True)
+    dq_t, dk_t, dv_t = fa.attn_bwd(q, kt, vt, out_t, lse_t, dout, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_t.view(torch.int16))
+    assert torch.equal(dq.view(torch.int16), dq_t.view(torch.int16))
+    assert torch.equal(dk[:, :, :Lb].view(torch.int16), dk_t.view(torch.int16))
+    assert torch.equal(dv[:, :, :Lb].view(torch.int16), dv_t.view(torch.int16))
+    assert bool((dk[:, :, Lb:].float() == 0).all()) and bool((dv[:, :, Lb:].float() == 0).all())
