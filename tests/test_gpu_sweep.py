@@ -182,3 +182,33 @@ def test_decode_with_extras(case):
     O_ref, lse_ref = _ref(x, _s32(d), causal, L, bias_bits)
     compare(to_f64(out), to_f64(lse), O_ref, lse_ref, BF16_MAX_ABS, BF16_MEAN_ABS,
             what=f"decode_ex {case} splits={n_splits}")
+
+
+BWD_EX = _shapes(9600, 8)
+
+
+@pytest.mark.parametrize("case", BWD_EX, ids=_ids)
+def test_backward_with_key_lengths(case):
+    # the forward with random per-batch key lengths, then its backward (attn_bwd_ex)
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    seed = 9600 + 5 * Nq + Nk
+    L = I.draw_seqlens(seed + 2, B, Nk, edges=True)
+    x = I.draw_qkv(seed, B, Hq, Hkv, Nq, Nk, d)
+    g_bits = I.draw_grad(seed + 1, (B, Hq, Nq, d))
+    q, k, v = upload(x)
+    dout = I.to_device(g_bits, "bf16")
+    lens = torch.as_tensor(np.asarray(L, np.int32), device="cuda")
+    say(f"sweep backward with lengths {case} lens={list(L)}")
+    out, lse = fa.attn_fwd_ex(q, k, v, causal=causal, scale=_s32(d), seqlens_k=lens)
+    dq, dk, dv = fa.attn_bwd(q, k, v, out, lse, dout, causal=causal, scale=_s32(d),
+                             seqlens_k=lens)
+    torch.cuda.synchronize()
+    g = I.bf16_bits_to_f32(g_bits).astype(np.float64)
+    ref = A.attention_backward_fp64(*x.as_f64(), g, _s32(d), causal, seqlens_k=L)
+    for name, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        a = to_f64(a)
+        scale = max(float(np.abs(r).max(initial=0.0)), GRAD_FLOOR)
+        err = np.abs(a - r)
+        assert np.all(np.isfinite(a)), name
+        assert float(err.max()) / scale <= GRAD_MAX_REL, f"{name} {case}"
+        assert float(err.mean()) / scale <= GRAD_MEAN_REL, f"{name} {case}"
