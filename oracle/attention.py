@@ -354,13 +354,15 @@ def _accumulate(acc: np.ndarray, x: np.ndarray) -> np.ndarray:
     return acc + x
 
 
-def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool, seqlens_k=None):
+def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool, seqlens_k=None,
+                            bias=None):
     """(dq [B,Hq,Nq,d], dk [B,Hkv,Nk,d], dv [B,Hkv,Nk,d]): the gradients of L = Σ dout ∘ O for
-    O = softmax(scale·q·kᵀ + causal mask)·v, in fp64, from the definition (see the module
+    O = softmax(scale·q·kᵀ + bias + causal mask)·v, in fp64, from the definition (see the module
     docstring).  With ``seqlens_k`` (the reading of ``attention_fp64``) element b has only its
     first seqlens_k[b] keys: the causal mask is aligned to the end of those, and the keys past
-    them, which do not take part in O, get zero gradients.  Small and medium inputs only: every
-    (batch, head) keeps its [Nq, Nk] matrices."""
+    them, which do not take part in O, get zero gradients.  ``bias`` (as in ``attention_fp64``) is
+    a constant: it shifts the scores, so it enters P, and no gradient is taken for it.  Small and
+    medium inputs only: every (batch, head) keeps its [Nq, Nk] matrices."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -370,6 +372,7 @@ def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool, seqlens_k
         raise ValueError(f"dout must have the shape of q {q.shape}, got {dout.shape}")
     scale = _resolve_scale(scale, d)
     L = _key_lengths(seqlens_k, B, Nk)
+    bview = _bias_view(bias, B, Hq, Nq, Nk)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -382,7 +385,8 @@ def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool, seqlens_k
         for hq in range(Hq):
             hkv = _kv_head(hq, Hq, Hkv)
             kh, vh, qh, doh = k[b, hkv, :Lb], v[b, hkv, :Lb], q[b, hq], dout[b, hq]
-            p, _, _ = _masked_softmax(_scores(qh, kh, scale), vis)
+            brows = None if bview is None else bview(b, hq)[:, :Lb]
+            p, _, _ = _masked_softmax(_row_scores(qh, kh, scale, brows), vis)
             dp = doh @ vh.T
             ds = _softmax_backward(p, dp)
             dq[b, hq] = scale * (ds @ kh)

@@ -554,6 +554,36 @@ def pin_bwd_varlen_finite_differences():
         assert np.all(grads[0][0] == 0), "no key: dq = 0"
 
 
+def pin_bwd_bias_finite_differences():
+    """With an additive bias (a per-(batch, head) one with -inf entries and a broadcast one, with
+    and without key lengths), every gradient element against a central difference of
+    L = Σ g ∘ O through the forward oracle with that bias (pinned above)."""
+    h = 1e-6
+    B, Hq, Hkv, Nq, Nk, d = 2, 2, 1, 3, 4, 3
+    q, k, v = _rand(740, B, Hq, Nq, d), _rand(741, B, Hkv, Nk, d), _rand(742, B, Hkv, Nk, d)
+    g = _rand(743, B, Hq, Nq, d)
+    full = _rand(744, B, Hq, Nq, Nk) * 2.0
+    full[0, 1, 2, 1] = -np.inf
+    full[1, 0, 0, :] = -np.inf  # a row with every key masked
+    shared = _rand(745, 1, 1, Nq, Nk)
+    for bias, causal, L in ((full, False, None), (full, True, None), (shared, True, [2, 4])):
+        def loss(q_, k_, v_):
+            O, _ = A.attention_fp64(q_, k_, v_, 0.8, causal, bias=bias, seqlens_k=L)
+            return float((O * g).sum())
+
+        grads = A.attention_backward_fp64(q, k, v, g, 0.8, causal, seqlens_k=L, bias=bias)
+        for t, (x, gx) in enumerate(zip((q, k, v), grads)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p, args_m = [q, k, v], [q, k, v]
+                args_p[t], args_m[t] = xp, xm
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(gx, num, 1e-7, f"bias finite differences causal={causal} tensor {'qkv'[t]}")
+
+
 def pin_bwd_shift_invariances():
     """Shifting every key by c leaves O unchanged (a row-constant score change), so Σ_j dK_j = 0;
     shifting every value by c shifts O by c on rows with a visible key, so Σ_j dV_j = Σ dO over
@@ -617,6 +647,7 @@ ALL_PINS = [
     pin_bias_neg_inf_is_mask,
     pin_bwd_finite_differences,
     pin_bwd_varlen_finite_differences,
+    pin_bwd_bias_finite_differences,
     pin_bwd_shift_invariances,
     pin_bwd_gqa_equals_repeated_heads,
 ]
