@@ -225,17 +225,19 @@ SDPA_FA2_API int attn_bwd(const void* q, const void* k, const void* v, const voi
              float scale, int causal, void* stream);
 
 /*
- * attn_bwd_ex -- attn_bwd for a forward that took per-batch key lengths (attn_fwd_ex with
- * seqlens_k and no bias).  seqlens_k has the meaning and checks of the extras above (device
- * int32 [B], 4-byte aligned, values clamped to [0, Nk]; NULL makes the call attn_bwd): element b
- * has only its first seqlens_k[b] keys, with the causal mask aligned to their end, and the K/V
- * rows past them, which take no part in the forward, get dk = dv = 0 (every row of dk and dv up
- * to Nk is written).  A forward with a bias has no backward here.  Other arguments and errors as
- * for attn_bwd; out and lse must come from the forward with the same lengths.
+ * attn_bwd_ex -- attn_bwd for a forward that took the extras (attn_fwd_ex): per-batch key
+ * lengths and an additive bias, with the meanings and checks of the extras above (NULL for
+ * either means none; both NULL makes the call attn_bwd).  With seqlens_k element b has only its
+ * first seqlens_k[b] keys, with the causal mask aligned to their end, and the K/V rows past them,
+ * which take no part in the forward, get dk = dv = 0 (every row of dk and dv up to Nk is
+ * written).  The bias enters P exactly as in the forward and is a constant: no gradient is
+ * computed for it.  Other arguments and errors as for attn_bwd; out and lse must come from the
+ * forward with the same extras.
  */
 SDPA_FA2_API int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out,
                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
                 void* workspace, size_t workspace_bytes, const int* seqlens_k,
+                const void* bias, int bias_b, int bias_h,
                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
                 float scale, int causal, void* stream);
 

@@ -35,7 +35,8 @@ _SIGNATURES = {
                      [_c_float, _c_int, _vp]),
     "attn_bwd_workspace_bytes": (_c_size, [_c_int] * 3),
     "attn_bwd": (_c_int, [_vp] * 10 + [_c_size] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
-    "attn_bwd_ex": (_c_int, [_vp] * 10 + [_c_size, _vp] + [_c_int] * 6 + [_c_float, _c_int, _vp]),
+    "attn_bwd_ex": (_c_int, [_vp] * 10 + [_c_size] + [_vp, _vp, _c_int, _c_int] + [_c_int] * 6 +
+                    [_c_float, _c_int, _vp]),
     "attn_status_string": (ctypes.c_char_p, [_c_int]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -303,11 +304,11 @@ def attn_forward(q, k, v, causal: bool = True, scale: float = 0.0, seqlens_k=Non
 
 
 def attn_bwd(q, k, v, out, lse, dout, causal: bool = True, scale: float = 0.0, dq=None, dk=None,
-             dv=None, workspace=None, seqlens_k=None):
+             dv=None, workspace=None, seqlens_k=None, bias=None):
     """Gradients (dq, dk, dv) of the forward on bf16 [B,H,N,d] tensors (d 64 or 128), given the
     forward's output and logsumexp and the gradient ``dout`` of the loss w.r.t. the output.  With
-    ``seqlens_k`` (int32 [B] on the device, as for ``attn_fwd_ex``) it is the backward of the
-    forward with those key lengths (``attn_bwd_ex``)."""
+    ``seqlens_k`` and / or ``bias`` (as for ``attn_fwd_ex``) it is the backward of the forward
+    with those extras (``attn_bwd_ex``; no gradient is taken for the bias)."""
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
@@ -328,11 +329,10 @@ def attn_bwd(q, k, v, out, lse, dout, causal: bool = True, scale: float = 0.0, d
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
             _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size())
     tail = (B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(q.device))
-    if seqlens_k is None:
+    if seqlens_k is None and bias is None:
         rc = load().attn_bwd(*head, *tail)
     else:
-        sp = _extras(q, B, Hq, Nq, Nk, seqlens_k, None)[0]
-        rc = load().attn_bwd_ex(*head, sp, *tail)
+        rc = load().attn_bwd_ex(*head, *_extras(q, B, Hq, Nq, Nk, seqlens_k, bias), *tail)
     _check_rc(rc, "attn_bwd")
     return dq, dk, dv
 
@@ -342,9 +342,9 @@ def attn_bwd_workspace_bytes(B: int, Hq: int, Nq: int) -> int:
 
 
 def prepare_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, causal: bool = True,
-                scale: float = 0.0, seqlens_k=None):
+                scale: float = 0.0, seqlens_k=None, bias=None):
     """A zero-argument callable that enqueues ``attn_bwd`` (``attn_bwd_ex`` with
-    ``seqlens_k``) with these tensors (timing loops)."""
+    ``seqlens_k`` or ``bias``) with these tensors (timing loops)."""
     import torch
 
     B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
@@ -356,11 +356,11 @@ def prepare_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, causal: bool = T
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
             _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size())
     tail = (B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(q.device))
-    if seqlens_k is None:
+    if seqlens_k is None and bias is None:
         fn, args = load().attn_bwd, head + tail
     else:
         fn = load().attn_bwd_ex
-        args = head + (_extras(q, B, Hq, Nq, Nk, seqlens_k, None)[0],) + tail
+        args = head + tuple(_extras(q, B, Hq, Nq, Nk, seqlens_k, bias)) + tail
 
     def call():
         rc = fn(*args)

@@ -214,14 +214,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              const void* dout, void* dq, void* dk, void* dv, void* workspace,
              size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
              int causal, void* stream) {
-  return attn_bwd_ex(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, nullptr, B,
-                     Hq, Hkv, Nq, Nk, d, scale, causal, stream);
+  return attn_bwd_ex(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, nullptr,
+                     nullptr, 1, 1, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream);
 }
 
 int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, const float* lse,
                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                size_t workspace_bytes, const int* seqlens_k, int B, int Hq, int Hkv, int Nq,
-                int Nk, int d, float scale, int causal, void* stream) {
+                size_t workspace_bytes, const int* seqlens_k, const void* bias, int bias_b,
+                int bias_h, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                int causal, void* stream) {
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d < 0) return ATTN_ERR_SHAPE;
   if (Nq >= kMaxSeq || Nk >= kMaxSeq) return ATTN_ERR_SHAPE;
   uint64_t tmp;
@@ -245,7 +246,10 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
     return ATTN_ERR_ALIGN;
   if (has_k && (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16)))
     return ATTN_ERR_ALIGN;
-  if (seqlens_k != nullptr && !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGN;
+  if (has_q || has_k) {
+    const int rc = check_extras(seqlens_k, bias, bias_b, bias_h, B, Hq, Nk);
+    if (rc != ATTN_OK) return rc;
+  }
   if (has_q) {
     const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
     if (need == 0 || workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
@@ -257,7 +261,8 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
     return ATTN_ERR_SHAPE;
   const fa::AttnShape s{B, Hq, Hkv, Nq, Nk, d};
   return launch_status(fa::launch_bwd_bf16(q, k, v, out, lse, dout, dq, dk, dv, (float*)workspace,
-                                           seqlens_k, s, resolve_scale(scale, d), causal != 0,
+                                           seqlens_k, bias, bias_b, bias_h, s,
+                                           resolve_scale(scale, d), causal != 0,
                                            (hipStream_t)stream));
 }
 

@@ -168,13 +168,13 @@ __device__ __forceinline__ void p_and_ds(float& s, float& dp, float c, float lse
 
 // ---------------------------------------------------------------------------------------------
 // dQ: workgroup = 4 waves = 128 query rows; 64-key blocks of K and V through LDS.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dQ,
-    const int* __restrict__ seqlens, int Hq, int Hkv, int Nq, int Nk_cap, int nqt, float scale,
-    float scale_log2) {
+    const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
+    int Hq, int Hkv, int Nq, int Nk_cap, int nqt, float scale, float scale_log2) {
   constexpr int TILE = Geo<D>::TILE, NCB = Geo<D>::NCB, NDB = Geo<D>::NDB;
   __shared__ __attribute__((aligned(1024))) uint16_t kl0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t kl1[TILE];
@@ -197,6 +197,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, min(Nq - 1, qt * 128 + 127) + off + 1);
   const int n_blk = kv_end > 0 ? (kv_end + BT - 1) / BT : 0;
+
+  // additive bias (bf16 [bias_b, bias_h, Nq, Nk_cap], batch / head dims broadcast when 1), added
+  // to the scores in score units (bias / scale), as in the forward.  A resource covers this
+  // wave's 32 rows (rows past Nq read zero); a lane loads its row's 4-key groups, 8 bytes each.
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(
+      BIAS ? bias + (((size_t)(bias_b == 1 ? 0 : b) * bias_h + (bias_h == 1 ? 0 : hq)) * Nq +
+                     (size_t)min(qw0, Nq)) * Nk_cap
+           : nullptr,
+      BIAS ? (uint32_t)max(0, min(32, Nq - qw0)) * Nk_cap * 2 : 0u);
+  const uint32_t b_lane = (uint32_t)l32 * Nk_cap * 2 + 8u * h;
+  const float inv_scale = 1.f / scale;
 
   // Q and dO of this lane's query as the B operand (dims 16c + 8h .. +7)
   u32x4 qf[NCB], gf[NCB];
@@ -242,6 +253,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const bool need = (k0 + BT > Nk) || (CAUSAL && (k0 + BT - 1 > qw0 + off));
     const int lim = CAUSAL ? min(Nk - 1, my_q + off) : Nk - 1;
     u32x4 pb[4];
+    u32x2 bw[8];  // bias of keys k0 + 32 (i >> 2) + 8 (i & 3) + 4 h .. +3, this lane's row
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        bw[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                    brs, (int)(b_lane + (uint32_t)(32 * (i >> 2) + 8 * (i & 3)) * 2), k0 * 2, 0));
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -253,6 +271,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float s0 = s[r], s1 = s[r + 1], d0 = dp[r], d1 = dp[r + 1];
+        if constexpr (BIAS) {
+          const uint32_t w = bw[4 * kb + (r >> 2)][(r >> 1) & 1];
+          s0 += __uint_as_float(w << 16) * inv_scale;
+          s1 += __uint_as_float(w & 0xffff0000u) * inv_scale;
+        }
         p_and_ds(s0, d0, scale_log2, lse2, dd);
         p_and_ds(s1, d1, scale_log2, lse2, dd);
         if (need) {
@@ -283,13 +306,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 // set and one accumulator set, and the two waves of a SIMD carry equal loads.  The dK waves work
 // one block behind the dV waves (the P of block t is read in step t + 1), so one barrier per step
 // orders everything: Q / dO / reference blocks are triple-buffered, P double-buffered.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, const int* __restrict__ seqlens, int Hq, int Hkv, int Nq,
-    int Nk_cap, int nkt, float scale, float scale_log2) {
+    uint16_t* __restrict__ dV, const int* __restrict__ seqlens, const uint16_t* __restrict__ bias,
+    int bias_b, int bias_h, int Hq, int Hkv, int Nq, int Nk_cap, int nkt, float scale,
+    float scale_log2) {
   constexpr int TILE = Geo<D>::TILE, NCB = Geo<D>::NCB, NDB = Geo<D>::NDB;
   __shared__ __attribute__((aligned(1024))) uint16_t qls[3][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gls[3][TILE];
@@ -363,6 +387,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     u32x4* const pw = pls[blk & 1] + pair * 4 * 64 + lane;  // this lane's operand slots (stride 64)
     const int q0 = (qb0 + blk % per_head) * BT;
     if (kw0 >= Nk || (CAUSAL && q0 + BT - 1 + off < kw0)) continue;  // nothing visible
+    // additive bias of this lane's key for the block's 64 query rows (dV waves only: the dK
+    // waves take P from them), entry 16 half + 4 g4 + e for row 32 half + 8 g4 + 4 h + e; a
+    // resource over the block's rows (rows past Nq read zero), requested before the first product
+    uint32_t bq[32];
+    if constexpr (BIAS) {
+      if (!do_k) {
+        const int g = blk / per_head;
+        const size_t row0 =
+            (((size_t)(bias_b == 1 ? 0 : b) * bias_h + (bias_h == 1 ? 0 : hkv * G + g)) * Nq +
+             (size_t)q0) * Nk_cap;
+        const __amdgpu_buffer_rsrc_t brs =
+            make_rsrc(bias + row0, (uint32_t)max(0, min(BT, Nq - q0)) * Nk_cap * 2);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t qrel = 32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * h + (i & 3);
+          bq[i] = __builtin_amdgcn_raw_buffer_load_b16(brs, (int)((qrel * Nk_cap + my_k) * 2), 0, 0);
+        }
+      }
+    }
     // first product for both 32-row halves, interleaved: S = Q K^T or dP = dO V^T; half j holds
     // queries q0 + 32 j + 8 (r >> 2) + 4 h + (r & 3) of this key
     f32x16 r2[2] = {f32x16{}, f32x16{}};
@@ -390,8 +433,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           for (int e = 0; e < 4; e += 2) {
             const int r = 4 * g4 + e;
             // (rows past Nq read a reference of 0 and are masked below)
-            float p0 = fast_exp2(fmaf(r2[half][r], scale_log2, -l4[e]));
-            float p1 = fast_exp2(fmaf(r2[half][r + 1], scale_log2, -l4[e + 1]));
+            float x0 = -l4[e], x1 = -l4[e + 1];
+            if constexpr (BIAS) {  // bias · log2e added to the exponent (bias / scale in scores)
+              x0 = fmaf(__uint_as_float(bq[16 * half + r] << 16), kLog2e, x0);
+              x1 = fmaf(__uint_as_float(bq[16 * half + r + 1] << 16), kLog2e, x1);
+            }
+            float p0 = fast_exp2(fmaf(r2[half][r], scale_log2, x0));
+            float p1 = fast_exp2(fmaf(r2[half][r + 1], scale_log2, x1));
             if (need) {
               const int q = q0 + qi + e;
               if (!(q < Nq && my_k < Nk && (!CAUSAL || my_k <= q + off))) p0 = 0.f;
@@ -440,10 +488,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
                   h);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS>
 hipError_t launch(const void* q, const void* k, const void* v, const void* out, const float* lse,
                   const void* dout, void* dq, void* dk, void* dv, float* ws_d, const int* seqlens,
-                  const AttnShape& s, float scale, hipStream_t stream) {
+                  const void* bias, int bias_b, int bias_h, const AttnShape& s, float scale,
+                  hipStream_t stream) {
   const long long rows = (long long)s.B * s.Hq * s.Nq;
   float* const ws_l2 = ws_d + rows;  // the workspace holds D, then the log2-unit references
   const int nqt = (s.Nq + 127) / 128, nkt = (s.Nk + 127) / 128;
@@ -460,39 +509,52 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
     if (e != hipSuccess) return e;
   }
   if (g_kv > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g_kv), dim3(512), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, BIAS>), dim3((unsigned)g_kv), dim3(512), 0,
+                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dk,
-                       (uint16_t*)dv, seqlens, s.Hq, s.Hkv, s.Nq, s.Nk, nkt, scale,
-                       scale * kLog2e);
+                       (uint16_t*)dv, seqlens, (const uint16_t*)bias, bias_b, bias_h, s.Hq, s.Hkv,
+                       s.Nq, s.Nk, nkt, scale, scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (g_dq > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g_dq), dim3(256), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, BIAS>), dim3((unsigned)g_dq), dim3(256), 0,
+                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dq,
-                       seqlens, s.Hq, s.Hkv, s.Nq, s.Nk, nqt, scale, scale * kLog2e);
+                       seqlens, (const uint16_t*)bias, bias_b, bias_h, s.Hq, s.Hkv, s.Nq, s.Nk, nqt,
+                       scale, scale * kLog2e);
     e = hipGetLastError();
   }
   return e;
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_b(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, float* ws_d,
+                    const int* seqlens, const void* bias, int bias_b, int bias_h,
+                    const AttnShape& s, float scale, hipStream_t stream) {
+  return bias ? launch<D, CAUSAL, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, bias,
+                                        bias_b, bias_h, s, scale, stream)
+              : launch<D, CAUSAL, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens,
+                                         nullptr, 1, 1, s, scale, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* out,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* ws_d, const int* seqlens, const AttnShape& s, float scale,
-                           bool causal, hipStream_t stream) {
+                           float* ws_d, const int* seqlens, const void* bias, int bias_b,
+                           int bias_h, const AttnShape& s, float scale, bool causal,
+                           hipStream_t stream) {
   if (s.d == 128)
-    return causal ? launch<128, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, s, scale,
-                                      stream)
-                  : launch<128, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, s,
-                                       scale, stream);
-  return causal ? launch<64, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, s, scale,
-                                   stream)
-                : launch<64, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, s, scale,
-                                    stream);
+    return causal ? launch_b<128, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, bias,
+                                        bias_b, bias_h, s, scale, stream)
+                  : launch_b<128, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, bias,
+                                         bias_b, bias_h, s, scale, stream);
+  return causal ? launch_b<64, true>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, bias,
+                                     bias_b, bias_h, s, scale, stream)
+                : launch_b<64, false>(q, k, v, out, lse, dout, dq, dk, dv, ws_d, seqlens, bias,
+                                      bias_b, bias_h, s, scale, stream);
 }
 
 }  // namespace fa

@@ -34,10 +34,12 @@ hipError_t launch_decode_splitkv(const void* q, const void* k, const void* v, vo
 
 // Backward (bwd_bf16.hip), head dim 64 or 128: D = rowsum(dout * out) into ws_d (fp32 [B, Hq, Nq]),
 // then dk/dv and dq; lse is the forward's natural-log logsumexp.  seqlens (device int32 [B], or
-// nullptr) limits batch element b to its first seqlens[b] keys, as in the forward.
+// nullptr) limits batch element b to its first seqlens[b] keys, and bias (bf16 [bias_b, bias_h,
+// Nq, Nk], or nullptr) is added to the scores, both as in the forward.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* out,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* ws_d, const int* seqlens, const AttnShape& s, float scale,
-                           bool causal, hipStream_t stream);
+                           float* ws_d, const int* seqlens, const void* bias, int bias_b,
+                           int bias_h, const AttnShape& s, float scale, bool causal,
+                           hipStream_t stream);
 
 }  // namespace fa

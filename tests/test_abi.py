@@ -255,13 +255,16 @@ def test_backward_validation(lib):
 
 def test_backward_with_lengths_validation(lib):
     # attn_bwd_ex checks what attn_bwd checks, plus the alignment of the length array
-    def bwd_ex(seqlens, **kw):
+    def bwd_ex(seqlens, bias=None, bias_b=1, bias_h=1, **kw):
         a = {**GOOD, **kw}
         return lib.attn_bwd_ex(A16, A16, A16, A16, A16, A16, A16, A16, A16, A16, 1 << 40, seqlens,
-                               a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
-                               a["causal"], None)
+                               bias, bias_b, bias_h, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                               a["d"], a["scale"], a["causal"], None)
 
     assert bwd_ex(A16 + 2) == C["ATTN_ERR_ALIGN"]
+    assert bwd_ex(None, bias=A16, bias_b=3) == C["ATTN_ERR_BIAS"]   # neither 1 nor B
+    assert bwd_ex(None, bias=A16, Nk=GOOD["Nk"] + 1) == C["ATTN_ERR_BIAS"]  # Nk % 4 != 0
+    assert bwd_ex(None, bias=A16 + 8) == C["ATTN_ERR_ALIGN"]
     assert bwd_ex(A16, d=96) == C["ATTN_ERR_HEADDIM"]
     assert bwd_ex(A16, Hq=3) == C["ATTN_ERR_GQA"]
     assert bwd_ex(None, B=0) == C["ATTN_OK"]

@@ -243,3 +243,40 @@ def test_backward_with_lengths_matches_truncated_tensors():
     assert torch.equal(dk[:, :, :Lb].view(torch.int16), dk_t.view(torch.int16))
     assert torch.equal(dv[:, :, :Lb].view(torch.int16), dv_t.view(torch.int16))
     assert bool((dk[:, :, Lb:].float() == 0).all()) and bool((dv[:, :, Lb:].float() == 0).all())
+
+
+# additive bias (attn_bwd_ex): (B, Hq, Hkv, Nq, Nk, d, causal, bias batch, bias heads, kind,
+# -inf fraction, lengths or None); Nk a multiple of 4 as the bias layout requires
+BIASED = [
+    (2, 4, 2, 130, 300, 128, True, 2, 4, "normal", 0.1, None),
+    (1, 4, 1, 257, 128, 128, False, 1, 4, "alibi", 0.0, None),
+    (3, 2, 2, 200, 200, 64, True, 1, 1, "normal", 0.0, [200, 0, 77]),
+    (2, 8, 2, 64, 520, 128, True, 2, 1, "alibi", 0.0, [520, 131]),
+    (2, 2, 1, 300, 132, 64, False, 2, 2, "normal", 0.2, [100, 132]),
+]
+
+
+@pytest.mark.parametrize("case", BIASED, ids=lambda c: "B{}_Hq{}_Hkv{}_Nq{}_Nk{}_d{}_{}_bias{}x{}_{}".format(
+    *c[:6], "causal" if c[6] else "full", c[7], c[8], c[9]))
+def test_backward_with_bias(case):
+    B, Hq, Hkv, Nq, Nk, d, causal, Bb, Hb, kind, masked, L = case
+    seed = 5100 + Nq + 3 * Nk + d
+    x = I.draw_qkv(seed, B, Hq, Hkv, Nq, Nk, d)
+    g_bits = I.draw_grad(seed + 1, (B, Hq, Nq, d))
+    bias_bits = I.draw_bias(seed + 2, Bb, Hb, Nq, Nk, kind, masked_frac=masked)
+    q, k, v = upload(x)
+    dout = I.to_device(g_bits, "bf16")
+    bias = I.to_device(bias_bits, "bf16")
+    lens = None if L is None else torch.as_tensor(np.asarray(L, np.int32), device="cuda")
+    s32 = _s32(d)
+    say(f"backward with bias {case}")
+    out, lse = fa.attn_fwd_ex(q, k, v, causal=causal, scale=s32, seqlens_k=lens, bias=bias)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    fa.attn_bwd(q, k, v, out, lse, dout, causal=causal, scale=s32, dq=dq, dk=dk, dv=dv,
+                seqlens_k=lens, bias=bias)
+    torch.cuda.synchronize()
+    g = I.bf16_bits_to_f32(g_bits).astype(np.float64)
+    ref = A.attention_backward_fp64(*x.as_f64(), g, s32, causal, seqlens_k=L,
+                                    bias=I.bf16_bits_to_f32(bias_bits).astype(np.float64))
+    for name, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        _check(name, to_f64(a), r)
