@@ -212,3 +212,36 @@ def test_backward_with_key_lengths(case):
         assert np.all(np.isfinite(a)), name
         assert float(err.max()) / scale <= GRAD_MAX_REL, f"{name} {case}"
         assert float(err.mean()) / scale <= GRAD_MEAN_REL, f"{name} {case}"
+
+
+BWD_BIAS = [_extras_case(c) for c in _shapes(9700, 8)]
+
+
+@pytest.mark.parametrize("case", BWD_BIAS, ids=_ids)
+def test_backward_with_extras(case):
+    # the forward with random key lengths and / or a random bias, then its backward
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    seed = 9700 + 11 * Nq + Nk
+    L, bias_bits = _extras_draw(case, seed)
+    x = I.draw_qkv(seed, B, Hq, Hkv, Nq, Nk, d)
+    g_bits = I.draw_grad(seed + 1, (B, Hq, Nq, d))
+    q, k, v = upload(x)
+    dout = I.to_device(g_bits, "bf16")
+    sl, bias = _dev_extras(L, bias_bits)
+    say(f"sweep backward_ex {case} lens={None if L is None else list(L)} "
+        f"bias={None if bias_bits is None else bias_bits.shape}")
+    out, lse = fa.attn_fwd_ex(q, k, v, causal=causal, scale=_s32(d), seqlens_k=sl, bias=bias)
+    dq, dk, dv = fa.attn_bwd(q, k, v, out, lse, dout, causal=causal, scale=_s32(d),
+                             seqlens_k=sl, bias=bias)
+    torch.cuda.synchronize()
+    g = I.bf16_bits_to_f32(g_bits).astype(np.float64)
+    ref = A.attention_backward_fp64(
+        *x.as_f64(), g, _s32(d), causal, seqlens_k=L,
+        bias=None if bias_bits is None else I.bf16_bits_to_f32(bias_bits).astype(np.float64))
+    for name, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        a = to_f64(a)
+        scale = max(float(np.abs(r).max(initial=0.0)), GRAD_FLOOR)
+        err = np.abs(a - r)
+        assert np.all(np.isfinite(a)), name
+        assert float(err.max()) / scale <= GRAD_MAX_REL, f"{name} {case}"
+        assert float(err.mean()) / scale <= GRAD_MEAN_REL, f"{name} {case}"
