@@ -213,17 +213,19 @@ def cpu_baseline(w, target_s: float):
 class Backward:
     """attn_bwd on a workload's inputs, after one forward call that provides out and LSE."""
 
-    def __init__(self, w, torch, fa, I):
+    def __init__(self, w, torch, fa, I, seqlens_k=None, bias=None):
         x = w.draw()
         self.q, self.k, self.v = (I.to_device(a, "bf16") for a in (x.q, x.k, x.v))
         self.dout = I.to_device(I.draw_grad(w.seed + 1, (w.B, w.Hq, w.Nq, w.d)), "bf16")
-        self.out, self.lse = fa.attn_fwd(self.q, self.k, self.v, causal=w.causal)
+        self.out, self.lse = fa.attn_fwd_ex(self.q, self.k, self.v, causal=w.causal,
+                                            seqlens_k=seqlens_k, bias=bias)
         self.dq, self.dk, self.dv = (torch.empty_like(t) for t in (self.q, self.k, self.v))
         ws = torch.empty(max(fa.attn_bwd_workspace_bytes(w.B, w.Hq, w.Nq), 16), dtype=torch.uint8,
                          device="cuda")
         self.ws = ws
         self.call = fa.prepare_bwd(self.q, self.k, self.v, self.out, self.lse, self.dout, self.dq,
-                                   self.dk, self.dv, ws, causal=w.causal)
+                                   self.dk, self.dv, ws, causal=w.causal, seqlens_k=seqlens_k,
+                                   bias=bias)
 
     def __call__(self, i):
         self.call()
@@ -251,6 +253,24 @@ def backward(torch, fab, I, W, steps, warmup, names=("prefill_causal_b2h16n2048"
         print(json.dumps(line), flush=True)
         del part
         torch.cuda.empty_cache()
+    # the backward of the forward extras on the B2 H16 N2048 causal workload: an ALiBi bias
+    # [1, H, N, N] (FLOPs as without it), and key lengths (FLOPs over the visible pairs)
+    w = W["prefill_causal_b2h16n2048"]
+    bias = I.to_device(I.draw_bias(1001, 1, w.Hq, w.Nq, w.Nk, "alibi"), "bf16")
+    L = I.draw_seqlens(1010, w.B, w.Nk, edges=False)
+    lens = torch.as_tensor(L, device="cuda")
+    vis_flops = 2.5 * sum(4.0 * w.Hq * w.d * visible_pairs(w.Nq, int(l), w.causal) for l in L)
+    for tag, kw, flops in (("bias_1x16_alibi", {"bias": bias}, bwd_flops(w)),
+                           ("varlen_" + "_".join(str(int(x)) for x in L), {"seqlens_k": lens},
+                            vis_flops)):
+        part = Backward(w, torch, fab, I, **kw)
+        _, (ms,) = time_steps(torch, [part], steps, warmup)
+        tf = flops / (ms * 1e-3) / 1e12
+        line = {"backward": w.name, "extra": tag, "mean_ms": round(ms, 5), "TFLOPS": round(tf, 1),
+                "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+        rows.append(line)
+        print(json.dumps(line), flush=True)
+        del part
     return rows
 
 
