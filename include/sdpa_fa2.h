@@ -21,7 +21,8 @@
  *          and Work Partitioning", code example).
  * Scale:   scores are multiplied by `scale` before masking; scale == 0 selects 1/sqrt(d) (the
  *          default of the WebGPU decode program, "[onnxruntime] WebGPU FlashAttention 최적화",
- *          section 2).  A negative or non-finite scale is rejected.
+ *          section 2).  A negative or non-finite scale, or a positive one below 2^-32, is
+ *          rejected (the kernels carry a bias as bias / scale, which must stay finite).
  * Causal:  when `causal` is non-zero, key j is visible to query i iff j <= i + (Nk - Nq), i.e. the
  *          mask is aligned to the end of the keys; with Nq == Nk it is the usual lower triangle.
  *          A query row with no visible key gets out = 0 and lse = -inf.
@@ -61,7 +62,7 @@ enum {
   ATTN_ERR_HEADDIM = -3,   /* d is not 64 or 128 */
   ATTN_ERR_GQA = -4,       /* Hkv < 1 while Hq > 0, or Hq % Hkv != 0 */
   ATTN_ERR_ALIGN = -5,     /* a tensor base address is not suitably aligned */
-  ATTN_ERR_SCALE = -6,     /* scale is negative, NaN or infinite */
+  ATTN_ERR_SCALE = -6,     /* scale is negative, NaN, infinite, or in (0, 2^-32) */
   ATTN_ERR_SPLITS = -7,    /* n_splits < 1 or n_splits > max(Nk, 1) */
   ATTN_ERR_WORKSPACE = -8, /* workspace NULL or smaller than its *_workspace_bytes() size */
   ATTN_ERR_LAUNCH = -9,    /* the HIP runtime rejected a kernel launch */
@@ -94,7 +95,14 @@ SDPA_FA2_API int attn_fwd_f32(const void* q, const void* k, const void* v, void*
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode_splitkv needs:
- *   B*Hq*Nq*n_splits*(d + 2)*4.  Returns 0 for invalid (negative) arguments.
+ *   B*Hq*Nq*n_splits*(d + 2)*4: one fp32 partial output row of d values plus the (local max,
+ *   local sum) pair per query row and split, the out_split_vx / metadata outputs of the fused
+ *   decode program of "[onnxruntime] WebGPU FlashAttention 최적화: 커널 퓨전과 가변 시퀀스 길이
+ *   지원으로 성능 극대화" (section 1).  The caller owns this memory, as a library workspace is
+ *   the caller's memory in "3.3 cuDNN II — 그래프 융합 API·휴리스틱" (section 3.3.2, the workspace
+ *   trade-off).
+ *   Host-only arithmetic, no device access.  Returns 0 for negative arguments or when the size
+ *   overflows size_t.
  */
 SDPA_FA2_API size_t attn_decode_workspace_bytes(int B, int Hq, int Nq, int d, int n_splits);
 
@@ -142,7 +150,7 @@ SDPA_FA2_API int attn_decode_splitkv(const void* q, const void* k, const void* v
  *            Nk must be a multiple of 4.  The bias is added to the scaled scores before the mask
  *            (s = scale * q.k + bias), the attention bias of the same page's fused decode program
  *            (section 1); a -inf entry masks its key.  With seqlens_k, bias columns at or past
- *            seqlens_k[b] are never read.  bias_b / bias_h are ignored when bias is NULL.
+ *            seqlens_k[b] are never used (their values do not matter).  bias_b / bias_h are ignored when bias is NULL.
  *
  * Errors added by the extras: ATTN_ERR_BIAS (dims or Nk % 4) and ATTN_ERR_ALIGN (alignment).
  */
@@ -241,7 +249,13 @@ SDPA_FA2_API int attn_bwd_ex(const void* q, const void* k, const void* v, const 
                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
                 float scale, int causal, void* stream);
 
-/* attn_status_string -- a static, NUL-terminated description of a status code. */
+/*
+ * attn_status_string -- a static, NUL-terminated English description of a status code returned
+ * by the entry points above (the counterpart of the Status that the onnxruntime WebGPU page's
+ * host functions return, "[onnxruntime] WebGPU FlashAttention 최적화: 커널 퓨전과 가변 시퀀스
+ * 길이 지원으로 성능 극대화", the ComputeFlashAttentionDecodeQKV code under section 3).  Host-only; never NULL; unknown
+ * codes give "unknown status".  The string is owned by the library and must not be freed.
+ */
 SDPA_FA2_API const char* attn_status_string(int status);
 
 #ifdef __cplusplus

@@ -11,7 +11,8 @@ kernels behind a small C ABI (``include/sdpa_fa2.h``):
   (``seqlens_k``) and an additive bias;
 * ``attn_forward`` -- one entry for any query length: split-KV below 32 query rows, prefill
   otherwise;
-* ``attn_bwd`` -- the gradients dq, dk, dv of the forward (head dim 128).
+* ``attn_bwd`` -- the gradients dq, dk, dv of the forward (head dims 64 and 128), also of the
+  forward with key lengths and a bias (the bias itself gets no gradient).
 
 The Python functions here only marshal torch tensors into the C ABI (``binding.py``).
 """

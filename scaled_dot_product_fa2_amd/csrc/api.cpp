@@ -12,6 +12,14 @@
 namespace {
 
 constexpr int kMaxSeq = 1 << 30;  // keeps every in-kernel index product inside 32/64-bit range
+// Smallest non-zero scale accepted.  The kernels carry an additive bias in units of the unscaled
+// dot product (bias / scale), so 1 / scale must stay finite with room to spare: with the floor,
+// bias / scale is finite for every |bias| < 2^96.
+constexpr float kMinScale = 0x1p-32f;
+
+bool scale_ok(float scale) {
+  return scale >= 0.f && isfinite(scale) && (scale == 0.f || scale >= kMinScale);
+}
 
 bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
@@ -37,7 +45,7 @@ int check_common(const void* q, const void* k, const void* v, const void* out, c
   // kernels' 32-bit buffer offsets
   if (((uint64_t)Nk + 128u) * (uint64_t)d * 2u > 0xffffffffull) return ATTN_ERR_SHAPE;
   if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return ATTN_ERR_GQA;
-  if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   if ((uint64_t)B * (uint64_t)Hq * (uint64_t)Nq == 0) {
     *empty = true;
     return ATTN_OK;
@@ -232,7 +240,7 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, co
       ((uint64_t)Nq + 128u) * (uint64_t)d * 2u > 0xffffffffull)
     return ATTN_ERR_SHAPE;
   if ((Hq > 0 || Hkv > 0) && (Hkv < 1 || Hq % Hkv != 0)) return ATTN_ERR_GQA;
-  if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  if (!scale_ok(scale)) return ATTN_ERR_SCALE;
   const bool has_q = (uint64_t)B * (uint64_t)Hq * (uint64_t)Nq > 0;
   const bool has_k = (uint64_t)B * (uint64_t)Hkv * (uint64_t)Nk > 0;
   if (!has_q && !has_k) return ATTN_OK;
@@ -274,7 +282,8 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
     case ATTN_ERR_GQA: return "Hq must be a positive multiple of Hkv";
     case ATTN_ERR_ALIGN: return "tensor base address is not suitably aligned";
-    case ATTN_ERR_SCALE: return "scale must be finite and >= 0 (0 selects 1/sqrt(d))";
+    case ATTN_ERR_SCALE:
+      return "scale must be 0 (selects 1/sqrt(d)) or a finite value >= 2^-32";
     case ATTN_ERR_SPLITS: return "n_splits must be in [1, max(Nk, 1)]";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL or too small";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";

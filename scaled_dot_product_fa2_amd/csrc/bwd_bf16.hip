@@ -1,4 +1,4 @@
-// Attention backward for gfx950, bf16 in/out, fp32 accumulation (head dim 128).
+// Attention backward for gfx950, bf16 in/out, fp32 accumulation (head dims 64 and 128).
 //
 // Not on the pages (they give only the speedups of the backward pass).  The gradients of
 // L = sum(dO * O) through O = softmax(scale * Q K^T + causal mask) V are, with P recomputed from

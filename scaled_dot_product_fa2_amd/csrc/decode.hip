@@ -32,6 +32,7 @@
 #include <math.h>
 
 namespace fa {
+
 namespace {
 
 constexpr long long kSimdCount = 1024;  // MI355X: 256 CUs x 4 SIMDs
@@ -138,13 +139,19 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 1 : 2) void decode_split_kernel(
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + split_off, split_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + split_off, split_bytes);
   // additive bias (bf16 [bias_b, bias_h, Nq, Nk_cap], broadcast over batch / heads when 1): a
-  // lane needs keys k0 + 16hh + 4grp + 0..3 of its own row, two 8-byte loads per block, issued
-  // with the block's K/V.  Groups of four never straddle a row (Nk_cap % 4 == 0); groups at or
-  // past the split end are not loaded (those keys are masked).
+  // lane needs keys key .. key+3 of its own row, key = ks0 + 32kb + 16hh + 4grp, for each of two
+  // groups per block, loaded with the block's K/V.  Every load is an aligned 8-byte unit of four
+  // keys [4u, 4u + 4): rows start 8-byte aligned (16-byte aligned base, Nk_cap % 4 == 0), so such
+  // a unit never crosses the end of the row.  key is congruent to the split start mod 4, so the
+  // misalignment a = ks0 mod 4 is the same for the whole workgroup: for a == 0 the group is one
+  // unit; otherwise it spans two units, the second loaded only when a key it supplies is inside
+  // the split, and the four keys are shifted out of the pair.  Keys at or past the split end
+  // are masked, so whatever a unit holds there is never used.
   const uint16_t* brow =
       BIAS ? bias + (((size_t)(bias_b == 1 ? 0 : b) * bias_h + (bias_h == 1 ? 0 : hq)) * Nq + qi) *
                         Nk_cap
            : nullptr;
+  const int bias_mis = ks0 & 3;  // misalignment of every group of this workgroup, in keys
   const float inv_scale = 1.f / scale;
   uint16_t* kls = (uint16_t*)smem + wave * C::WTILE;
   uint16_t* vls = kls + C::KB * D;
@@ -163,8 +170,12 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 1 : 2) void decode_split_kernel(
     if constexpr (BIAS) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int key = ks0 + C::KB * kb + 16 * hh + 4 * grp;
-        bst[hh] = (row_ok && key < ks1) ? *(const u32x2*)(brow + key) : u32x2{0u, 0u};
+        const int unit = ks0 + C::KB * kb + 16 * hh + 4 * grp - bias_mis;  // a multiple of 4
+        uint64_t lo = 0, hi = 0;
+        if (row_ok && unit + bias_mis < ks1) lo = *(const uint64_t*)(brow + unit);
+        if (row_ok && bias_mis != 0 && unit + 4 < ks1) hi = *(const uint64_t*)(brow + unit + 4);
+        const uint64_t w = bias_mis == 0 ? lo : (lo >> (16 * bias_mis)) | (hi << (64 - 16 * bias_mis));
+        bst[hh] = __builtin_bit_cast(u32x2, w);
       }
     }
   };

@@ -2,6 +2,8 @@
 and compare against the CPU fp64 oracle element by element."""
 from __future__ import annotations
 
+import concurrent.futures
+import os
 import sys
 
 import numpy as np
@@ -68,3 +70,41 @@ def sample_rows(Nq: int, n_random: int = 16, seed: int = 0) -> np.ndarray:
     rnd = np.random.default_rng(seed).integers(0, Nq, size=n_random)
     rows = np.array(sorted({int(r) for r in list(fixed) + list(rnd) if 0 <= r < Nq}))
     return rows
+
+
+def oracle_threads() -> int:
+    """Worker threads for the oracle: the host cores this process may run on, at most 16 (the
+    CPU share a one-GPU machine grants a job)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_full(q, k, v, scale: float, causal: bool, row_chunk: int = 2048):
+    """The oracle's O and LSE over every element of a (large) problem, computed as independent
+    tasks of (batch, query head, row chunk) on a thread pool with single-threaded BLAS per task.
+
+    Each task is ``attention_rows_fp64`` on that slice's K/V head and those query positions (the
+    oracle's own row function, whose rows are exact rows of the full result: the causal mask uses
+    each row's true position), so nothing here changes what the oracle computes."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as A
+
+    B, Hq, Nq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, Nq, d))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    tasks = [(b, h, r0) for b in range(B) for h in range(Hq) for r0 in range(0, Nq, row_chunk)]
+
+    def one(task):
+        b, h, r0 = task
+        rows = np.arange(r0, min(Nq, r0 + row_chunk))
+        o, l = A.attention_rows_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1],
+                                     v[b:b + 1, h // G:h // G + 1], scale, causal, rows)
+        out[b, h, rows] = o[0, 0]
+        lse[b, h, rows] = l[0, 0]
+
+    with threadpool_limits(limits=1):
+        with concurrent.futures.ThreadPoolExecutor(max_workers=oracle_threads()) as ex:
+            list(ex.map(one, tasks))
+    return out, lse

@@ -97,6 +97,11 @@ def test_forward_validation(lib, f32):
     assert _fwd(lib, f32=f32, scale=float("nan")) == C["ATTN_ERR_SCALE"]
     assert _fwd(lib, f32=f32, scale=float("inf")) == C["ATTN_ERR_SCALE"]
     assert _fwd(lib, f32=f32, scale=-0.5) == C["ATTN_ERR_SCALE"]
+    # positive scales below 2^-32 (subnormals among them) are refused: 1/scale must stay finite
+    # for the bias, which the kernels carry in units of the unscaled dot product
+    assert _fwd(lib, f32=f32, scale=2.0**-33) == C["ATTN_ERR_SCALE"]
+    assert _fwd(lib, f32=f32, scale=1e-45) == C["ATTN_ERR_SCALE"]
+    assert _fwd(lib, f32=f32, scale=2.0**-32, lse=A16 + 2) == C["ATTN_ERR_ALIGN"]  # accepted
     assert _fwd(lib, f32=f32, q=None) == C["ATTN_ERR_NULL"]
     assert _fwd(lib, f32=f32, o=None) == C["ATTN_ERR_NULL"]
     assert _fwd(lib, f32=f32, k=None) == C["ATTN_ERR_NULL"]
@@ -121,6 +126,7 @@ def test_decode_validation(lib):
     assert _dec(lib, Hq=6, Hkv=4) == C["ATTN_ERR_GQA"]
     assert _dec(lib, q=None) == C["ATTN_ERR_NULL"]
     assert _dec(lib, scale=float("-inf")) == C["ATTN_ERR_SCALE"]
+    assert _dec(lib, scale=3e-39) == C["ATTN_ERR_SCALE"]  # subnormal
     assert _dec(lib, B=0, q=None, k=None, v=None, o=None, ws=None) == C["ATTN_OK"]
 
 
@@ -238,6 +244,7 @@ def test_backward_validation(lib):
     assert _bwd(lib, B=-1) == C["ATTN_ERR_SHAPE"]
     assert _bwd(lib, Hq=3) == C["ATTN_ERR_GQA"]
     assert _bwd(lib, scale=float("nan")) == C["ATTN_ERR_SCALE"]
+    assert _bwd(lib, scale=2.0**-40) == C["ATTN_ERR_SCALE"]
     for name in ("lse", "dout", "dq", "q", "o", "k", "v", "dk", "dv"):
         assert _bwd(lib, **{name: None}) == C["ATTN_ERR_NULL"], name
     assert _bwd(lib, dq=A16 + 8) == C["ATTN_ERR_ALIGN"]
