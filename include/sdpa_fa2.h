@@ -11,7 +11,8 @@
  * Memory:  every tensor pointer is a DEVICE pointer (HIP device memory, or memory the device can
  *          address).  The caller allocates and frees every buffer, including the decode
  *          workspace; the library never allocates, frees or synchronises, and keeps no state
- *          beyond its loaded code objects.
+ *          beyond its loaded code objects (which include the fixed scratch array of
+ *          attn_decode_splitkv_noalloc) and that entry point's cached per-device address of it.
  * Layout:  contiguous row-major tensors in the native [batch, heads, seq, head_dim] order
  *          ("BNSH"), head_dim fastest:  q, out: [B, Hq, Nq, d];  k, v: [B, Hkv, Nk, d];
  *          lse: [B, Hq, Nq] float32.  No transposes are taken or required.
@@ -66,7 +67,8 @@ enum {
   ATTN_ERR_SPLITS = -7,    /* n_splits < 1 or n_splits > max(Nk, 1) */
   ATTN_ERR_WORKSPACE = -8, /* workspace NULL or smaller than its *_workspace_bytes() size */
   ATTN_ERR_LAUNCH = -9,    /* the HIP runtime rejected a kernel launch */
-  ATTN_ERR_BIAS = -10      /* bias_b not 1 or B, bias_h not 1 or Hq, or Nk % 4 != 0 with a bias */
+  ATTN_ERR_BIAS = -10,     /* bias_b not 1 or B, bias_h not 1 or Hq, or Nk % 4 != 0 with a bias */
+  ATTN_ERR_SCRATCH = -11   /* attn_decode_splitkv_noalloc: the partials exceed its fixed scratch */
 };
 
 /*
@@ -131,6 +133,29 @@ SDPA_FA2_API int attn_decode_splitkv(const void* q, const void* k, const void* v
                         void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int Nq, int Nk, int d,
                         float scale, int causal, int n_splits, void* stream);
+
+/*
+ * attn_decode_splitkv_noalloc -- attn_decode_splitkv for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, layouts, kernels and results as attn_decode_splitkv (bit-identical), without
+ * the workspace pair: the split partials go to a fixed 32 MiB array of device memory inside the
+ * library instead (one per GPU, held from the library's first use of that GPU until the process
+ * ends).  The call allocates and frees nothing: the array's device address is looked up once per
+ * device (on the first call whose stream is on that device) and cached.
+ *   Limit: attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits) <= 33,554,432 bytes, else
+ *   ATTN_ERR_SCRATCH and nothing is enqueued (e.g. B=8, Hq=32, Nq=4, d=128, 16 splits needs
+ *   8,519,680 bytes).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents (each call
+ * overwrites every partial it reads, so nothing needs clearing first).  Calls that may overlap on
+ * one GPU -- on different streams without ordering, or from several threads -- race on the array
+ * and must not be issued; calls on one stream are ordered.  ATTN_ERR_LAUNCH also reports a failed
+ * address lookup.
+ */
+SDPA_FA2_API int attn_decode_splitkv_noalloc(const void* q, const void* k, const void* v,
+                                             void* out, float* lse, int B, int Hq, int Hkv,
+                                             int Nq, int Nk, int d, float scale, int causal,
+                                             int n_splits, void* stream);
 
 /*
  * Extras of the *_ex entry points and of attn_forward (all optional: NULL means "none").

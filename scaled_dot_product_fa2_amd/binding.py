@@ -29,6 +29,8 @@ _SIGNATURES = {
                     [_c_float, _c_int, _vp]),
     "attn_decode_splitkv_ex": (_c_int, [_vp] * 6 + [_c_size] + [_vp, _vp, _c_int, _c_int] +
                                [_c_int] * 6 + [_c_float, _c_int, _c_int, _vp]),
+    "attn_decode_splitkv_noalloc": (_c_int, [_vp] * 5 + [_c_int] * 6 +
+                                    [_c_float, _c_int, _c_int, _vp]),
     "attn_decode_num_splits": (_c_int, [_c_int] * 5),
     "attn_forward_workspace_bytes": (_c_size, [_c_int] * 6),
     "attn_forward": (_c_int, [_vp] * 6 + [_c_size] + [_vp, _vp, _c_int, _c_int] + [_c_int] * 6 +
@@ -271,6 +273,22 @@ def attn_decode_splitkv_ex(q, k, v, n_splits: int, causal: bool = True, scale: f
                                        int(bool(causal)), int(n_splits), _stream(q.device))
     _check_rc(rc, "attn_decode_splitkv_ex")
     return out, lse, workspace
+
+
+def attn_decode_splitkv_noalloc(q, k, v, n_splits: int, causal: bool = True, scale: float = 0.0,
+                                out=None, lse=None, want_lse: bool = True):
+    """Split-KV decode through the entry point that allocates nothing (its partials live in the
+    library's fixed device scratch); returns (out, lse).  Pass ``out`` (and ``lse``) to keep the
+    whole call free of allocations."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nk, d = _validate(q, k, v, torch.bfloat16)
+    out, lse = _out_lse(q, B, Hq, Nq, out, lse, want_lse)
+    rc = load().attn_decode_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B,
+                                            Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                                            int(n_splits), _stream(q.device))
+    _check_rc(rc, "attn_decode_splitkv_noalloc")
+    return out, lse
 
 
 def attn_decode_num_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int) -> int:

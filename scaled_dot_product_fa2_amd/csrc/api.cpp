@@ -179,6 +179,23 @@ int attn_decode_splitkv_ex(const void* q, const void* k, const void* v, void* ou
                     bias_h, B, Hq, Hkv, Nq, Nk, d, scale, causal, n_splits, empty, stream);
 }
 
+int attn_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* out,
+                                float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                float scale, int causal, int n_splits, void* stream) {
+  bool empty;
+  int rc = check_common(q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, d, scale, &empty);
+  if (rc != ATTN_OK) return rc;
+  if (n_splits < 1 || n_splits > (Nk > 1 ? Nk : 1)) return ATTN_ERR_SPLITS;
+  if (empty) return ATTN_OK;
+  const size_t need = attn_decode_workspace_bytes(B, Hq, Nq, d, n_splits);
+  if (need == 0 || need > fa::kDecodeScratchBytes) return ATTN_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (fa::decode_scratch_address((hipStream_t)stream, &scratch) != hipSuccess)
+    return ATTN_ERR_LAUNCH;
+  return run_decode(q, k, v, out, lse, scratch, fa::kDecodeScratchBytes, nullptr, nullptr, 1, 1,
+                    B, Hq, Hkv, Nq, Nk, d, scale, causal, n_splits, false, stream);
+}
+
 int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0) return 1;
   // enough workgroups to give every compute unit a few (4 x 256), but at least 256 keys (two
@@ -289,6 +306,8 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
     case ATTN_ERR_BIAS:
       return "bias dims must be 1 or B (batch) and 1 or Hq (heads), and Nk a multiple of 4";
+    case ATTN_ERR_SCRATCH:
+      return "the split partials need more than the library's fixed 32 MiB decode scratch";
     default: return "unknown status";
   }
 }

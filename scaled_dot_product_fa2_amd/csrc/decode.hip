@@ -31,7 +31,15 @@
 
 #include <math.h>
 
+#include <atomic>
+
 namespace fa {
+
+// Workspace of attn_decode_splitkv_noalloc, for callers that cannot allocate: a fixed array in
+// the code object, one copy per device (each GPU the library runs on holds it until the process
+// ends).  Host code never uses its name as an address (in host code the name is a host-side
+// stand-in); the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 
 namespace {
 
@@ -509,6 +517,34 @@ hipError_t launch_b(const void* q, const void* k, const void* v, void* out, floa
 }
 
 }  // namespace
+
+hipError_t decode_scratch_address(hipStream_t stream, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cached[kMaxDevices];
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // the symbol's address on `dev`, taken with that device current (two threads racing here
+    // both store the same address)
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = dev != cur ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cached[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_decode_splitkv(const void* q, const void* k, const void* v, void* out,
                                  float* lse, float* ws_o, float* ws_ml, const int* seqlens,

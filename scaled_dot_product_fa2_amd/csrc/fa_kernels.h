@@ -32,6 +32,13 @@ hipError_t launch_decode_splitkv(const void* q, const void* k, const void* v, vo
                                  const void* bias, int bias_b, int bias_h, const AttnShape& s,
                                  float scale, bool causal, int n_splits, hipStream_t stream);
 
+// Bytes of the fixed device scratch array behind attn_decode_splitkv_noalloc (decode.hip).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+
+// Device address of that array on the device of `stream` (the current device for the NULL
+// stream), looked up once per device with hipGetSymbolAddress and cached.  Allocates nothing.
+hipError_t decode_scratch_address(hipStream_t stream, void** ptr);
+
 // Backward (bwd_bf16.hip), head dim 64 or 128: D = rowsum(dout * out) into ws_d (fp32 [B, Hq, Nq]),
 // then dk/dv and dq; lse is the forward's natural-log logsumexp.  seqlens (device int32 [B], or
 // nullptr) limits batch element b to its first seqlens[b] keys, and bias (bf16 [bias_b, bias_h,
