@@ -3,21 +3,33 @@
 
 One step is one pass over the whole hot path on seeded synthetic bf16 inputs already resident
 in HBM:
-  * prefill: attn_fwd on B=2, H=16, N=2048, d=128, causal (the headline workload);
+  * prefill (attn_fwd, causal, d=128): B=1, H=8, N=16384 (the headline workload: causal
+    prefill at N >= 4096), then B=4, H=16, N=4096 (the longest sequence of the N 512-4096 sweep)
+    and B=2, H=16, N=2048;
   * decode:  attn_decode_splitkv (split kernel + combine kernel) on B=8, Hq=32, Hkv=8, Nk=8192,
              d=128, n_splits=16, once with Nq=1 and once with Nq=4.  Four distinct K/V buffer sets
              (4 x 268 MB) are rotated so the 256 MB MALL cannot serve repeated reads.
 
-The timed region runs exactly K steps, grouped by part: the K prefill launches back to back, then
-the K decode (Nq=1) calls, then the K decode (Nq=4) calls, each group between one pair of HIP
-events recorded on the stream the library launches on (torch's current stream).  Per-launch event
-pairs were avoided because each adds about 5 us of marker overhead.  The calls are marshalled once
-before the timed region so that host-side overhead cannot leave the GPU idle inside a bracket.  The printed JSON line carries:
-  value      prefill TFLOPS (4*B*H*N^2*d / 2 for causal, over the prefill kernel's mean time);
-  decode     HBM GB/s of the split + combine pair over the algorithmic bytes (K and V once, Q, O,
-             LSE), for Nq=1 and Nq=4;
-  roofline   the prefill kernel against the bf16 dense MFMA peak (and decode against 8 TB/s);
-  cpu_baseline  the CPU fp64 oracle timed on a bounded sample of the prefill workload.
+Before the W warm-up steps the parts run round-robin for --settle-s seconds (default 1): an idle
+MI355X takes a large fraction of a second to raise its clock, far longer than a few warm-up
+steps of this hot path.  The timed region then runs exactly K steps, grouped by part: part j's K launches run back to back in
+a few brackets (4 when K >= 4), each bracket between one pair of HIP events recorded on the
+stream the library launches on (torch's current stream), and the device is synchronised between
+parts.  Per-launch event pairs were avoided because each adds about 5 us of marker overhead.  The
+calls are marshalled once before the timed region so that host-side overhead cannot leave the GPU
+idle inside a bracket.  The printed JSON line carries:
+  value         TFLOPS of the headline prefill (4*B*H*N^2*d / 2 for causal, over the mean time
+                per launch of all K launches);
+  prefill_extra the same for the other two prefill workloads;
+  decode        HBM GB/s of each split + combine pair over the algorithmic bytes (K and V once,
+                Q, O, LSE), for Nq=1 and Nq=4;
+  roofline      the headline prefill kernel against the bf16 dense MFMA peak (each extra
+                workload and decode pair carries its own: MFMA, or 8 TB/s HBM);
+  min_ms, median_ms  the fastest and the median bracket of each part (mean per launch);
+  device       the device name, compute units and ROCm version;
+  clock         the shader clock under each part's load: a spin kernel of known cycle count
+                timed beside an untimed repetition of the part (null when it did not overlap);
+  cpu_baseline  the CPU fp64 oracle timed on a bounded sample of each workload.
 
 Options: --sweep prints one extra line per prefill/decode workload; --extras prints one line per
 variant with per-batch key lengths or an additive bias (see ``extras``); --bwd prints one line per
@@ -32,7 +44,9 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -41,8 +55,10 @@ sys.path.insert(0, ROOT)
 METRIC = ("causal bf16 attn fwd TFLOPS (% MFMA peak); decode split-KV HBM GB/s (% peak)")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-HEADLINE = "prefill_causal_b2h16n2048"
+HEADLINE = "long_causal_b1h8n16384"
+PREFILL_EXTRA = ("sweep_n4096_b4_causal", "prefill_causal_b2h16n2048")
 DECODE = ("decode_gqa_nq1", "decode_gqa_nq4")
+BRACKETS = 4
 KV_SETS = 4
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "scaled_dot_product_fa2_amd", "csrc")
@@ -138,34 +154,114 @@ def decode_kv_sets(torch, I, w, n):
     return sets
 
 
-def time_steps(torch, parts, steps, warmup):
-    """Run warmup untimed steps, then exactly `steps` steps.  The timed region is grouped by part:
-    part j runs its `steps` launches back to back between one pair of events on the current
-    stream, then part j+1 follows.  (An event pair around every single launch adds about 5 us of
-    marker overhead per bracket on this stack, which would inflate each kernel's time.)
-    Returns (wall ms per step, [mean ms per launch of each part])."""
+def clock_during(torch, part, steps, part_ms):
+    """The shader clock while `part` runs, from a separate, untimed repetition of its `steps`
+    launches: a spin kernel that waits a known number of shader-clock cycles runs beside them on
+    a second stream (one wave, next to the part's waves), and HIP events on that stream time it.
+    The estimate counts only when the spin ended before the part did (so it ran under the load
+    throughout); otherwise it is reported as null.  Returns (MHz or None, spin ms, part ms)."""
+    cycles = int(max(part_ms * steps, 0.2) * 1e-3 * 0.5 * 1.0e9)  # half the part at 1 GHz
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(side):  # the spin is queued first, so it is dispatched first
+        e0.record(side)
+        torch.cuda._sleep(cycles)
+        e1.record(side)
+    m0.record()
+    for i in range(steps):
+        part(i)
+    m1.record()
+    torch.cuda.synchronize()
+    spin_ms, run_ms = e0.elapsed_time(e1), m0.elapsed_time(m1)
+    inside = m0.elapsed_time(e1) <= run_ms and e0.elapsed_time(m0) >= -0.05
+    mhz = round(cycles / (spin_ms * 1e3), 1) if inside and spin_ms > 0 else None
+    return mhz, round(spin_ms, 4), round(run_ms, 4)
+
+
+def settle(torch, parts, seconds):
+    """Run the parts round-robin for `seconds` of wall time before the warm-up steps: an idle
+    GPU takes a large fraction of a second to raise its clock (a 5-step warm-up of this hot path
+    is ~5 ms), so without this the first parts would be timed while the clock still ramps."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for p in parts:
+            p(n)
+        n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def _bracket_sizes(steps, brackets):
+    n = max(1, min(brackets, steps))
+    return [steps // n + (1 if r < steps % n else 0) for r in range(n)]
+
+
+def time_parts(torch, parts, names, steps, warmup, brackets=BRACKETS, settle_s=0.0, clock=False):
+    """Run the parts for `settle_s` seconds (see ``settle``), then `warmup` untimed steps, then
+    exactly `steps` steps grouped by part: part j runs its `steps` launches back to back, split
+    into up to `brackets` brackets that each sit between one pair of events on the current
+    stream; the device is synchronised between parts.  (An event pair around every single
+    launch adds about 5 us of marker overhead on this stack, which would inflate each kernel's
+    time.)  With `clock`, each part is then repeated once, untimed, beside a spin kernel that
+    measures the shader clock under that load (``clock_during``).  Returns (wall ms per step,
+    {name: stats}) with stats holding the mean per launch over all `steps` launches, the min /
+    median of the bracket means and the clock."""
+    settle_steps = settle(torch, parts, settle_s) if settle_s > 0 else 0
     for i in range(warmup):
         for p in parts:
             p(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in parts]
+    sizes = _bracket_sizes(steps, brackets)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in sizes] for _ in parts]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t_all = time.perf_counter()
     for j, p in enumerate(parts):
-        ev[j][0].record()
-        for i in range(steps):
-            p(i)
-        ev[j][1].record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    means = [ev[j][0].elapsed_time(ev[j][1]) / steps for j in range(len(parts))]
-    return wall_ms, means
+        i = 0
+        for r, n in enumerate(sizes):
+            evs[j][r][0].record()
+            for _ in range(n):
+                p(i)
+                i += 1
+            evs[j][r][1].record()
+        torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_all) * 1e3 / steps
+    stats = {}
+    for j, name in enumerate(names):
+        tot = [evs[j][r][0].elapsed_time(evs[j][r][1]) for r in range(len(sizes))]
+        per = [t / n for t, n in zip(tot, sizes)]
+        stats[name] = {"mean_ms": sum(tot) / steps, "min_ms": min(per),
+                       "median_ms": statistics.median(per), "brackets": len(sizes),
+                       "settle_steps": settle_steps}
+    if clock:
+        for j, name in enumerate(names):
+            mhz, spin_ms, run_ms = clock_during(torch, parts[j], steps, stats[name]["mean_ms"])
+            stats[name]["clock"] = {"mhz": mhz, "spin_ms": spin_ms, "part_ms": run_ms}
+    return wall_ms, stats
 
 
-def cpu_baseline(w, target_s: float):
-    """The CPU fp64 oracle, unmodified, over a bounded sample of (batch, head) slices of the
-    workload, one slice per worker thread with single-threaded BLAS."""
+def time_steps(torch, parts, steps, warmup):
+    """time_parts without names: (wall ms per step, [mean ms per launch of each part])."""
+    names = [f"part{j}" for j in range(len(parts))]
+    wall, st = time_parts(torch, parts, names, steps, warmup)
+    return wall, [st[n]["mean_ms"] for n in names]
+
+
+def oracle_cores():
+    """Threads for the CPU baseline: every core this process may run on, at most 16 (the host
+    CPU share a one-GPU job is granted on the GPU machines, whatever the node's core count)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(w, seconds: float, cores: int):
+    """The CPU fp64 oracle, unmodified, on a bounded sample of the workload: tasks of (batch,
+    query head, up to 1024 query rows), each the oracle's row function on that slice, run on
+    `cores` threads with single-threaded BLAS, for about `seconds` of wall time.  Returns the
+    rate scaled to the whole workload (TFLOPS in the FLOP convention for prefill, GB/s of
+    algorithmic bytes for decode) and a description of the sample."""
     import concurrent.futures
 
     import numpy as np
@@ -176,38 +272,38 @@ def cpu_baseline(w, target_s: float):
     x = w.draw()
     q, k, v = x.as_f64()
     scale = float(np.float32(w.scale))
-    slices = [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    G = w.Hq // w.Hkv
+    chunk = min(1024, w.Nq)
+    tasks = [(b, h, r0) for r0 in range(0, w.Nq, chunk) for b in range(w.B) for h in range(w.Hq)]
 
-    def one(bh):
-        b, h = bh
-        hk = h // (w.Hq // w.Hkv)
-        A.attention_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1],
-                         scale, w.causal)
+    def one(t):
+        b, h, r0 = t
+        rows = np.arange(r0, min(w.Nq, r0 + chunk))
+        A.attention_rows_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1],
+                              v[b:b + 1, h // G:h // G + 1], scale, w.causal, rows)
+        return len(rows)
 
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        one(slices[0])
-        per_slice = time.perf_counter() - t0
-        # about target_s seconds of CPU work: a prefix of the slices when one pass is longer,
-        # else whole passes over every slice
-        want = max(1, round(target_s / max(per_slice, 1e-6)))
-        if want >= len(slices):
-            passes = max(1, want // len(slices))
-            sample = slices * passes
-            what = f"{passes} pass(es) over all {len(slices)} (batch, head) slices"
-        else:
-            sample = slices[:max(cores, want)]
-            what = f"{len(sample)} of {len(slices)} (batch, head) slices"
+        one(tasks[0])
+        per_task = time.perf_counter() - t0
+        want = max(cores, int(seconds * cores / max(per_task, 1e-6)))
+        # spread the sample over the tensor: every stride-th task
+        stride = max(1, len(tasks) // want)
+        sample = tasks[::stride][:want]
         t0 = time.perf_counter()
         with concurrent.futures.ThreadPoolExecutor(max_workers=cores) as ex:
-            list(ex.map(one, sample))
+            rows = sum(ex.map(one, sample))
         wall = time.perf_counter() - t0
-    flops = w.flops() * len(sample) / len(slices)
-    return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOPS", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{what} of {w.name}, all rows of each, numpy fp64, {wall:.1f} s wall on "
-                      f"{cores} threads"}
+    share = rows / (w.B * w.Hq * w.Nq)
+    if w.n_splits:
+        rate, unit = algorithmic_bytes(w) * share / wall / 1e9, "GB/s"
+    else:
+        rate, unit = w.flops() * share / wall / 1e12, "TFLOPS"
+    what = (f"{len(sample)} of {len(tasks)} (batch, head, {chunk}-row) tasks of {w.name} "
+            f"({100 * share:.2f}% of its rows), numpy fp64, {wall:.1f} s wall on {cores} threads")
+    return {"value": round(rate, 6), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": what}
 
 
 class Backward:
@@ -289,7 +385,7 @@ def extras(torch, fab, I, W, steps, warmup, kv):
         only the visible (query, key) pairs of each element;
       * decode (Nq=1 and Nq=4) with a length mix over the 8192-key capacity (GB/s over the K/V
         rows that exist) and with a per-head bias [1, Hq, Nq, Nk] (its bytes counted)."""
-    w = W[HEADLINE]
+    w = W["prefill_causal_b2h16n2048"]
     rows = []
 
     def prefill_line(name, part, flops, extra_bytes):
@@ -351,6 +447,19 @@ def roofline_hbm(nbytes, ms, traffic):
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic}
 
 
+def device_record(torch):
+    p = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "rocm": rocm,
+            "hip_runtime": torch.version.hip}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,7 +471,10 @@ def main():
     ap.add_argument("--bwd", action="store_true", help="also print one line per backward workload")
     ap.add_argument("--only", default=None, help="run only this workload (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warm-up, so the clock has ramped")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="CPU oracle wall seconds per reported workload")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run a plain device-to-device copy of this many bytes and exit")
     args = ap.parse_args()
@@ -409,47 +521,77 @@ def main():
         print(json.dumps({"workload": args.only, "mean_ms": round(ms, 5), "steps": args.steps}))
         return
 
-    prefill = Prefill(W[HEADLINE], torch, fab, I)
+    prefill_names = (HEADLINE, *PREFILL_EXTRA)
+    prefills = [Prefill(W[n], torch, fab, I) for n in prefill_names]
     kv = decode_kv_sets(torch, I, W[DECODE[0]], KV_SETS)
     decodes = [Decode(W[n], torch, fab, I, kv) for n in DECODE]
+    names = (*prefill_names, *DECODE)
     torch.cuda.synchronize()
-    wall_ms, means = time_steps(torch, [prefill, *decodes], args.steps, args.warmup)
-    pre_ms, dec_ms = means[0], means[1:]
+    wall_ms, st = time_parts(torch, [*prefills, *decodes], names, args.steps, args.warmup,
+                             settle_s=args.settle_s, clock=True)
 
-    w = W[HEADLINE]
-    tflops = w.flops() / (pre_ms * 1e-3) / 1e12
+    def r5(x):
+        return round(x, 5)
+
+    def prefill_obj(name):
+        w, t = W[name], st[name]
+        tf = w.flops() / (t["mean_ms"] * 1e-3) / 1e12
+        return {"value": round(tf, 2), "unit": "TFLOPS", "mean_ms": r5(t["mean_ms"]),
+                "min_ms": r5(t["min_ms"]), "median_ms": r5(t["median_ms"]),
+                "shape": {"B": w.B, "H": w.Hq, "N": w.Nq, "d": w.d, "causal": w.causal},
+                "roofline": roofline_mfma(w.flops(), t["mean_ms"],
+                                          measured_traffic("prefill", name)),
+                "clock": t["clock"]}
+
+    head = prefill_obj(HEADLINE)
     decode_obj = {}
-    for name, ms in zip(DECODE, dec_ms):
-        wd = W[name]
+    for name in DECODE:
+        wd, t = W[name], st[name]
         nbytes = algorithmic_bytes(wd)
         decode_obj[name] = {
-            "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "mean_ms": round(ms, 5),
-            "algorithmic_bytes": nbytes,
-            "roofline": roofline_hbm(nbytes, ms, measured_traffic("decode", name)),
+            "value": round(nbytes / (t["mean_ms"] * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "mean_ms": r5(t["mean_ms"]), "min_ms": r5(t["min_ms"]),
+            "median_ms": r5(t["median_ms"]), "algorithmic_bytes": nbytes,
+            "roofline": roofline_hbm(nbytes, t["mean_ms"], measured_traffic("decode", name)),
+            "clock": t["clock"],
         }
+    w = W[HEADLINE]
     line = {
         "metric": METRIC,
-        "value": round(tflops, 2),
+        "value": head["value"],
         "unit": "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_ms, 5),
+        "ms_per_step": r5(wall_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{HEADLINE} + {DECODE[0]} + {DECODE[1]}",
-                   "prefill": {"B": w.B, "H": w.Hq, "N": w.Nq, "d": w.d, "causal": w.causal},
+        "config": {"workload": HEADLINE,
+                   "prefill": head["shape"],
+                   "step_also_runs": [*PREFILL_EXTRA, *DECODE],
                    "decode": {"B": 8, "Hq": 32, "Hkv": 8, "Nq": [1, 4], "Nk": 8192, "d": 128,
-                              "n_splits": 16, "kv_buffer_sets": KV_SETS}},
-        "prefill_mean_ms": round(pre_ms, 5),
-        "roofline": roofline_mfma(w.flops(), pre_ms, measured_traffic("prefill", HEADLINE)),
+                              "n_splits": 16, "kv_buffer_sets": KV_SETS},
+                   "timing": f"{args.steps} launches per part in "
+                             f"{len(_bracket_sizes(args.steps, BRACKETS))} event brackets, after "
+                             f"{args.settle_s:g} s of settling and {args.warmup} warm-up steps",
+                   "settle_steps": st[HEADLINE]["settle_steps"]},
+        "prefill_mean_ms": head["mean_ms"],
+        "prefill_min_ms": head["min_ms"],
+        "prefill_median_ms": head["median_ms"],
+        "roofline": head["roofline"],
+        "clock": head["clock"],
+        "prefill_extra": {n: prefill_obj(n) for n in PREFILL_EXTRA},
         "decode": decode_obj,
+        "device": device_record(torch),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        cores = oracle_cores()
+        per = {n: cpu_baseline(W[n], args.cpu_seconds, cores) for n in names}
+        line["cpu_baseline"] = {**per[HEADLINE],
+                                "per_workload": {n: per[n] for n in names if n != HEADLINE}}
     print(json.dumps(line), flush=True)
 
     if args.extras:
@@ -460,27 +602,18 @@ def main():
 
     if args.sweep:
         for name, wk in W.items():
-            if wk.dtype != "bf16" or name == HEADLINE:
+            if wk.dtype != "bf16" or name in names:
                 continue
             if wk.n_splits:
-                part = decodes[DECODE.index(name)] if name in DECODE else None
-                if part is None:
-                    continue
-                _, (ms,) = time_steps(torch, [part], args.steps, args.warmup)
-                nbytes = algorithmic_bytes(wk)
-                print(json.dumps({"workload": name, "mean_ms": round(ms, 5),
-                                  "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                                  "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}),
-                      flush=True)
-            else:
-                part = Prefill(wk, torch, fab, I)
-                _, (ms,) = time_steps(torch, [part], args.steps, args.warmup)
-                tf = wk.flops() / (ms * 1e-3) / 1e12
-                print(json.dumps({"workload": name, "mean_ms": round(ms, 5),
-                                  "TFLOPS": round(tf, 1),
-                                  "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
-                del part
-                torch.cuda.empty_cache()
+                continue
+            part = Prefill(wk, torch, fab, I)
+            _, (ms,) = time_steps(torch, [part], args.steps, args.warmup)
+            tf = wk.flops() / (ms * 1e-3) / 1e12
+            print(json.dumps({"workload": name, "mean_ms": round(ms, 5),
+                              "TFLOPS": round(tf, 1),
+                              "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+            del part
+            torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

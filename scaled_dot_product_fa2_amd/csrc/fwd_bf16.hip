@@ -38,7 +38,10 @@
 //     with their 16-byte chunks XOR-swizzled, K and V each with the swizzle that makes its read
 //     pattern conflict-free on the 64 LDS banks.
 //   * Workgroups are ordered heaviest-first under the causal mask, and all query blocks of one
-//     (batch, head) are kept on one XCD so their shared K/V stays in that XCD's L2.
+//     (batch, head) are kept on one XCD so their shared K/V stays in that XCD's L2.  When the grid
+//     spans several rounds of workgroups, a workgroup instead takes query blocks nqt-1-i and i of
+//     one head in turn (equal causal work per workgroup), heads in order within each XCD, so the
+//     workgroups of a head start together and stream its K/V through L2 side by side.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -48,6 +51,8 @@
 
 namespace fa {
 namespace {
+
+constexpr long long kPairedMinGrid = 512;  // MI355X: 256 CUs x 2 workgroups
 
 template <int D>
 struct FwdCfg {
@@ -96,12 +101,13 @@ __device__ __forceinline__ void map_block(int n, int BH, int nqt, int& bh, int& 
   }
 }
 
+// One query block (bh, qt) of the forward: the whole FlashAttention-2 loop over its K/V blocks.
 template <int D, bool CAUSAL, bool BIAS>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__device__ __forceinline__ void fwd_tile(
+    int bh, int qt, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
-    int Hq, int Hkv, int Nq, int Nk_cap, int nqt, float scale, float scale_log2) {
+    int Hq, int Hkv, int Nq, int Nk_cap, float scale, float scale_log2) {
   using C = FwdCfg<D>;
   constexpr int NC = D / 16;  // 16-element head-dim slices per QK product
   __shared__ __attribute__((aligned(1024))) uint16_t kl0[C::TILE];
@@ -115,9 +121,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int BH = gridDim.x / nqt;
-  int bh, qt;
-  map_block(blockIdx.x, BH, nqt, bh, qt);
   const int b = bh / Hq, hq = bh - b * Hq;
   const int hkv = hq / (Hq / Hkv);
   // keys of this batch element: all Nk_cap rows of K/V, or the first seqlens[b] (clamped)
@@ -304,15 +307,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     }
   };
 
-  // exponent arguments x = s·scale·log2e - mb of score pair (j, j+1), in place, and their max
+  // exponent arguments x = s·scale·log2e - mb of score pair (j, j+1), in place, and their max.
+  // The running max takes one three-input max per pair (a chain of v_max3, 16 per block of 32
+  // arguments; the compiler's own reduction of the same expression used 24 operations).
   auto arg_pair = [&](f32x16 (&s)[2], float& amax, float mb, int j) {
     const int kb = j >> 4, r = j & 15;
     const float x0 = fmaf(s[kb][r], scale_log2, -mb);
     const float x1 = fmaf(s[kb][r + 1], scale_log2, -mb);
-    amax = fmaxf(amax, fmaxf(x0, x1));
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(amax) : "v"(amax), "v"(x0), "v"(x1));
     s[kb][r] = x0;
     s[kb][r + 1] = x1;
-    asm volatile("" ::"v"(x0), "v"(x1));  // keeps this work here, between the matrix products
   };
   // probabilities 2^x of pair (j, j+1), in place, packed into P
   auto exp_pair = [&](f32x16 (&s)[2], u32x4 (&pb)[4], int j) {
@@ -586,6 +590,38 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   }
 }
 
+// Paired grids (several rounds of workgroups): workgroup n runs on XCD n % 8 and takes, among
+// that XCD's heads in order, head slot / np's query blocks nqt-1-i and i (i = slot % np, np =
+// ceil(nqt / 2)), one after the other.  Every workgroup then carries the same causal work, and the
+// workgroups of one head start together, so they stream its K/V through the XCD's L2 at the same
+// time.  Other grids take one query block per workgroup (map_block).
+template <int D, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
+    int Hq, int Hkv, int Nq, int Nk_cap, int nqt, int BH, int paired, float scale,
+    float scale_log2) {
+  int bh, qt, qt2 = -1;
+  if (paired) {
+    const int np = (nqt + 1) / 2, hx = BH >> 3;
+    const int slot = blockIdx.x >> 3;
+    bh = (blockIdx.x & 7) * hx + slot / np;
+    const int i = slot % np;
+    qt = nqt - 1 - i;
+    if (i != qt) qt2 = i;
+  } else {
+    map_block(blockIdx.x, BH, nqt, bh, qt);
+  }
+  fwd_tile<D, CAUSAL, BIAS>(bh, qt, Q, K, V, O, LSE, seqlens, bias, bias_b, bias_h, Hq, Hkv, Nq,
+                            Nk_cap, scale, scale_log2);
+  if (qt2 >= 0) {
+    __syncthreads();  // every wave is done with the first block's LDS buffers
+    fwd_tile<D, CAUSAL, BIAS>(bh, qt2, Q, K, V, O, LSE, seqlens, bias, bias_b, bias_h, Hq, Hkv,
+                              Nq, Nk_cap, scale, scale_log2);
+  }
+}
+
 template <int D, bool CAUSAL, bool BIAS>
 hipError_t launch(const void* q, const void* k, const void* v, void* out, float* lse,
                   const int* seqlens, const void* bias, int bias_b, int bias_h,
@@ -594,10 +630,15 @@ hipError_t launch(const void* q, const void* k, const void* v, void* out, float*
   const int nqt = (s.Nq + C::BR - 1) / C::BR;
   const long long blocks = (long long)s.B * s.Hq * nqt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BIAS>), dim3((unsigned)blocks), dim3(C::NT), 0,
-                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                     (uint16_t*)out, lse, seqlens, (const uint16_t*)bias, bias_b, bias_h, s.Hq,
-                     s.Hkv, s.Nq, s.Nk, nqt, scale, scale * kLog2e);
+  const int BH = s.B * s.Hq;
+  // pair query blocks when even the paired grid fills every slot of the chip (256 CUs x 2)
+  const long long pairs = (long long)BH * ((nqt + 1) / 2);
+  const int paired = (BH % 8 == 0 && nqt > 1 && pairs >= kPairedMinGrid) ? 1 : 0;
+  const unsigned grid = paired ? (unsigned)pairs : (unsigned)blocks;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BIAS>), dim3(grid), dim3(C::NT), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out,
+                     lse, seqlens, (const uint16_t*)bias, bias_b, bias_h, s.Hq, s.Hkv, s.Nq,
+                     s.Nk, nqt, BH, paired, scale, scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -150,8 +150,8 @@ def test_prefill_bias_rising_max(slope, causal):
     rows = np.linspace(0.0, 3.0, Nq, dtype=np.float32)[None, None, :, None]
     bits = I.bf16_bits_from_f32(np.broadcast_to(ramp + rows, (1, 1, Nq, Nk)))
     out, lse, O_ref, lse_ref = _prefill(B, Hq, Hkv, Nq, Nk, d, causal, 660, bias_bits=bits)
+    # rows' LSE reach ~1300 at slope 2; the plain 1e-3 bound holds (measured at most 3.4e-4)
     compare(out, lse, O_ref, lse_ref, BF16_MAX_ABS, BF16_MEAN_ABS,
-            lse_tol=1e-3 + 4 * 2.0**-23 * float(np.abs(lse_ref[np.isfinite(lse_ref)]).max()),
             what=f"rising bias slope={slope} causal={causal}")
 
 
