@@ -156,26 +156,33 @@ def decode_kv_sets(torch, I, w, n):
 
 def clock_during(torch, part, steps, part_ms):
     """The shader clock while `part` runs, from a separate, untimed repetition of its `steps`
-    launches: a spin kernel that waits a known number of shader-clock cycles runs beside them on
-    a second stream (one wave, next to the part's waves), and HIP events on that stream time it.
+    launches: once the first launch is done, a spin kernel that waits a known number of
+    shader-clock cycles runs beside the others on a second stream (one wave, next to the part's
+    waves), and HIP events on that stream time it.
     The estimate counts only when the spin ended before the part did (so it ran under the load
     throughout); otherwise it is reported as null.  Returns (MHz or None, spin ms, part ms)."""
-    cycles = int(max(part_ms * steps, 0.2) * 1e-3 * 0.5 * 1.0e9)  # half the part at 1 GHz
+    cycles = int(max(part_ms * (steps - 1), 0.2) * 1e-3 * 0.5 * 1.0e9)  # half the rest at 1 GHz
     side = torch.cuda.Stream()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(side):  # the spin is queued first, so it is dispatched first
-        e0.record(side)
-        torch.cuda._sleep(cycles)
-        e1.record(side)
+    first = torch.cuda.Event()
     m0.record()
     for i in range(steps):
         part(i)
+        if i == 0:
+            first.record()
+            # the spin starts once the part's first launch is done, i.e. under the load of the
+            # following launches
+            side.wait_event(first)
+            with torch.cuda.stream(side):
+                e0.record(side)
+                torch.cuda._sleep(cycles)
+                e1.record(side)
     m1.record()
     torch.cuda.synchronize()
     spin_ms, run_ms = e0.elapsed_time(e1), m0.elapsed_time(m1)
-    inside = m0.elapsed_time(e1) <= run_ms and e0.elapsed_time(m0) >= -0.05
+    inside = m0.elapsed_time(e1) <= run_ms
     mhz = round(cycles / (spin_ms * 1e3), 1) if inside and spin_ms > 0 else None
     return mhz, round(spin_ms, 4), round(run_ms, 4)
 
