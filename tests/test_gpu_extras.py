@@ -139,6 +139,21 @@ def test_prefill_bias_and_varlen_together():
                 what=f"bias+varlen causal={causal}")
 
 
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, True)])
+def test_prefill_paired_grid_with_extras(d, causal):
+    # a grid of several rounds of workgroups runs paired query blocks (blocks nqt-1-i and i in
+    # one workgroup); here with an odd number of query blocks (9: the middle one runs alone),
+    # GQA, per-batch key lengths (the capacity, 0, 1 and a ragged one) and a per-head bias with
+    # -inf entries, full tensors against the oracle
+    B, Hq, Hkv, Nq, Nk = 4, 32, 8, 1100, 1100
+    assert B * Hq * ((Nq + 127) // 128 + 1) // 2 >= 512  # the paired grid is taken
+    L = I.draw_seqlens(650 + d, B, Nk)
+    bits = I.draw_bias(651 + d, 1, Hq, Nq, Nk, "normal", 2.0, 0.05)
+    out, lse, O_ref, lse_ref = _prefill(B, Hq, Hkv, Nq, Nk, d, causal, 652 + d, L=L, bias_bits=bits)
+    compare(out, lse, O_ref, lse_ref, BF16_MAX_ABS, BF16_MEAN_ABS,
+            what=f"paired grid d={d} causal={causal} lens={list(L)}")
+
+
 @pytest.mark.parametrize("slope", [0.02, 0.5, 2.0])
 @pytest.mark.parametrize("causal", [False, True])
 def test_prefill_bias_rising_max(slope, causal):
