@@ -245,7 +245,7 @@ SDPA_FA2_API size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  *   out, dout [B, Hq, Nq, d] bf16: the forward output and the gradient of the loss w.r.t. it
  *   lse [B, Hq, Nq] fp32: the forward's logsumexp (required; -inf rows get zero gradients)
  *   workspace: at least attn_bwd_workspace_bytes(B, Hq, Nq) bytes of device memory owned by the
- *     caller: fp32 D [B, Hq, Nq], then lse * log2(e) [B, Hq, Nq] (+inf for -inf rows), both
+ *     caller: fp32 -D [B, Hq, Nq], then -lse / scale [B, Hq, Nq] (-inf for -inf rows), both
  *     overwritten; calls that share it must be stream ordered.
  * scale and causal must be those of the forward call.  Keys that no query sees get dk = dv = 0;
  * with Nq == 0 and Nk > 0 the call writes zeros to dk and dv.  Errors as for attn_fwd (Nq, like

@@ -9,7 +9,8 @@
 // value heads shared by several query heads receive the sum over those heads.
 //
 // gfx950 mapping, three launches on one stream:
-//   * bwd_prep_kernel: D for every query row (16 lanes per row).
+//   * bwd_prep_kernel: per query row -D and -LSE / scale (the row terms), which start the
+//     accumulators of the score products so that they end as dP - D and S - LSE / scale.
 //   * bwd_dq_kernel: the forward's structure.  A workgroup owns 128 query rows (32 per wave, Q
 //     and dO held in registers as the B operand); 64-key blocks of K and V stream HBM -> LDS.
 //     S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 put one query per lane, so P and
@@ -29,6 +30,7 @@
 
 #include <math.h>
 
+#include <type_traits>
 namespace fa {
 namespace {
 
@@ -127,15 +129,17 @@ __device__ __forceinline__ void store_rowT(uint16_t* row_ptr, const f32x16 (&acc
     }
 }
 
-// D[row] = sum_d dO[row][d] * O[row][d] (D/8 lanes per row, 8 dims each), and the row's
-// reference for P in log2 units, L2[row] = LSE[row] * log2(e), +inf for a row with no visible key
-// (LSE = -inf) so that every P of it is exactly 0.
+// Per query row, negated so that they can start the accumulators of the score products:
+// Dn[row] = -sum_d dO[row][d] * O[row][d] (D/8 lanes per row, 8 dims each), and
+// Ln[row] = -LSE[row] / scale, the row's reference in score units, or -inf for a row with no
+// visible key (LSE = -inf) so that every P of it is exactly 0.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O,
                                                        const uint16_t* __restrict__ dO,
                                                        const float* __restrict__ LSE,
-                                                       float* __restrict__ Dd,
-                                                       float* __restrict__ L2, long long rows) {
+                                                       float* __restrict__ Dn,
+                                                       float* __restrict__ Ln, long long rows,
+                                                       float scale) {
   constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per row, rows per workgroup
   const long long row = (long long)blockIdx.x * RPB + (threadIdx.x / LPR);
   const int sub = threadIdx.x % LPR;
@@ -152,9 +156,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 #pragma unroll
   for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, LPR);
   if (row < rows && sub == 0) {
-    Dd[row] = acc;
+    Dn[row] = -acc;
     const float l = LSE[row];
-    L2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+    Ln[row] = l == -INFINITY ? -INFINITY : -l / scale;
   }
 }
 
@@ -172,7 +176,7 @@ template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dQ,
+    const float* __restrict__ Ln, const float* __restrict__ Dn, uint16_t* __restrict__ dQ,
     const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
     int Hq, int Hkv, int Nq, int Nk_cap, int nqt, float scale, float scale_log2) {
   constexpr int TILE = Geo<D>::TILE, NCB = Geo<D>::NCB, NDB = Geo<D>::NDB;
@@ -198,8 +202,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   if (CAUSAL) kv_end = min(Nk, min(Nq - 1, qt * 128 + 127) + off + 1);
   const int n_blk = kv_end > 0 ? (kv_end + BT - 1) / BT : 0;
 
-  // additive bias (bf16 [bias_b, bias_h, Nq, Nk_cap], batch / head dims broadcast when 1), added
-  // to the scores in score units (bias / scale), as in the forward.  A resource covers this
+  // additive bias (bf16 [bias_b, bias_h, Nq, Nk_cap], batch / head dims broadcast when 1), taken
+  // off the row's reference in log2 units (bias log2e), which adds bias / scale to the scores.  A resource covers this
   // wave's 32 rows (rows past Nq read zero); a lane loads its row's 4-key groups, 8 bytes each.
   const __amdgpu_buffer_rsrc_t brs = make_rsrc(
       BIAS ? bias + (((size_t)(bias_b == 1 ? 0 : b) * bias_h + (bias_h == 1 ? 0 : hq)) * Nq +
@@ -207,7 +211,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
            : nullptr,
       BIAS ? (uint32_t)max(0, min(32, Nq - qw0)) * Nk_cap * 2 : 0u);
   const uint32_t b_lane = (uint32_t)l32 * Nk_cap * 2 + 8u * h;
-  const float inv_scale = 1.f / scale;
 
   // Q and dO of this lane's query as the B operand (dims 16c + 8h .. +7)
   u32x4 qf[NCB], gf[NCB];
@@ -221,11 +224,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       gf[c] = ok ? *(const u32x4*)(grow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  // the row's reference in log2 units (+inf: no visible key, so every P is 0) and D
+  // the row's reference in log2 units, LSE log2e (+inf: no visible key, so every P is 0), and D
   float lse2 = INFINITY, dd = 0.f;
   if (my_q < Nq) {
-    lse2 = L2[(size_t)bh * Nq + my_q];
-    dd = Dd[(size_t)bh * Nq + my_q];
+    lse2 = -Ln[(size_t)bh * Nq + my_q] * scale_log2;
+    dd = -Dn[(size_t)bh * Nq + my_q];
   }
 
   const TileLanes tl = tile_lanes<D>(lane);
@@ -237,16 +240,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     copy_tile<D>(kg, 0, Nk, kl0, wave, lane);
     copy_tile<D>(vg, 0, Nk, vl0, wave, lane);
   }
-  for (int t = 0; t < n_blk; ++t) {
-    const uint16_t* kc = (t & 1) ? kl1 : kl0;
-    const uint16_t* vc = (t & 1) ? vl1 : vl0;
+  // step t reads buffer BUF = t % 2 and copies block t + 1 into the other one; the buffers are
+  // named at compile time so that the compiler sees that the copies and the reads touch
+  // different arrays (otherwise it waits for the copies before the transposing reads)
+  auto step = [&](auto buf_tag, int t) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const uint16_t* const kc = BUF ? kl1 : kl0;
+    const uint16_t* const vc = BUF ? vl1 : vl0;
     wait_vmem();
     __syncthreads();  // block t is in LDS; the other buffers are free
     if (t + 1 < n_blk) {
-      copy_tile<D>(kg, (t + 1) * BT, Nk, (t & 1) ? kl0 : kl1, wave, lane);
-      copy_tile<D>(vg, (t + 1) * BT, Nk, (t & 1) ? vl0 : vl1, wave, lane);
+      copy_tile<D>(kg, (t + 1) * BT, Nk, BUF ? kl0 : kl1, wave, lane);
+      copy_tile<D>(vg, (t + 1) * BT, Nk, BUF ? vl0 : vl1, wave, lane);
     }
-    if (qw0 >= Nq || (CAUSAL && t * BT > qw0 + 31 + off)) continue;
+    if (qw0 >= Nq || (CAUSAL && t * BT > qw0 + 31 + off)) return;
     // S^T = K Q^T and dP^T = V dO^T, 32 keys at a time (keys 32 kb + 8 (r >> 2) + 4 h + (r & 3)
     // of this query), each half turned into its dS^T operands before the next is computed
     const int k0 = t * BT;
@@ -271,13 +278,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float s0 = s[r], s1 = s[r + 1], d0 = dp[r], d1 = dp[r + 1];
-        if constexpr (BIAS) {
+        float l0 = lse2, l1 = lse2;
+        if constexpr (BIAS) {  // bias · log2e taken off the reference (bias / scale in scores)
           const uint32_t w = bw[4 * kb + (r >> 2)][(r >> 1) & 1];
-          s0 += __uint_as_float(w << 16) * inv_scale;
-          s1 += __uint_as_float(w & 0xffff0000u) * inv_scale;
+          l0 = fmaf(__uint_as_float(w << 16), -kLog2e, lse2);
+          l1 = fmaf(__uint_as_float(w & 0xffff0000u), -kLog2e, lse2);
         }
-        p_and_ds(s0, d0, scale_log2, lse2, dd);
-        p_and_ds(s1, d1, scale_log2, lse2, dd);
+        p_and_ds(s0, d0, scale_log2, l0, dd);
+        p_and_ds(s1, d1, scale_log2, l1, dd);
         if (need) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
           if (key > lim) d0 = 0.f;
@@ -293,13 +301,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         acc[db] = mfma32x32x16(read_tr<D>(kc, tl.tr_base, 16 * g, db), pb[g], acc[db]);
+  };
+  for (int t = 0; t < n_blk; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_blk) step(std::integral_constant<int, 1>{}, t + 1);
   }
   if (my_q < Nq) store_rowT<D>(dQ + ((size_t)bh * Nq + my_q) * D, acc, scale, h);
 }
 
 // ---------------------------------------------------------------------------------------------
-// dK and dV: workgroup = 8 waves for 128 keys; 64-row blocks of Q, dO and their references and D
-// go through LDS once for all of them, for every query head of the K/V head's group.  Waves w and
+// dK and dV: workgroup = 8 waves for 128 keys; 64-row blocks of Q, dO and their row terms go
+// through LDS once for all of them, for every query head of the K/V head's group.  Waves w and
 // w + 4 share 32 keys: wave w computes S = Q K^T, turns it into P and accumulates dV^T += dO^T P;
 // wave w + 4 computes dP = dO V^T, takes P from wave w through LDS and accumulates
 // dK^T += Q^T dS.  So every wave runs two of the four products per block and holds one operand
@@ -310,14 +322,14 @@ template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ L2, const float* __restrict__ Dd, uint16_t* __restrict__ dK,
+    const float* __restrict__ Ln, const float* __restrict__ Dn, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, const int* __restrict__ seqlens, const uint16_t* __restrict__ bias,
     int bias_b, int bias_h, int Hq, int Hkv, int Nq, int Nk_cap, int nkt, float scale,
     float scale_log2) {
   constexpr int TILE = Geo<D>::TILE, NCB = Geo<D>::NCB, NDB = Geo<D>::NDB;
   __shared__ __attribute__((aligned(1024))) uint16_t qls[3][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t gls[3][TILE];
-  __shared__ __attribute__((aligned(16))) float sls[3][2 * BT];  // reference (log2 units), then D
+  __shared__ __attribute__((aligned(16))) float sls[3][2 * BT];  // -LSE / scale, then -D
   // P of each wave pair as packed bf16 operands: [buffer][pair][operand i][lane], 16 bytes each,
   // so that a wave's 16-byte stores and loads of one operand cover 1 KB contiguously
   __shared__ __attribute__((aligned(1024))) u32x4 pls[2][4 * 4 * 64];
@@ -359,11 +371,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       copy_tile<D>(Q + bh * Nq * D, qb * BT, Nq, qls[buf], wave, lane);
     else
       copy_tile<D>(dO + bh * Nq * D, qb * BT, Nq, gls[buf], wave - 4, lane);
-    if (wave == 0) {  // 64 references then 64 D, four bytes per lane; rows past Nq read zero
+    if (wave == 0) {  // 64 -LSE / scale then 64 -D, four bytes per lane; rows past Nq read zero
       const int q = qb * BT;
       const uint32_t n = (uint32_t)max(0, Nq - q) * 4;
-      load_lds_4(make_rsrc(L2 + bh * Nq + min(q, Nq), n), sls[buf], (uint32_t)lane * 4);
-      load_lds_4(make_rsrc(Dd + bh * Nq + min(q, Nq), n), sls[buf] + BT, (uint32_t)lane * 4);
+      load_lds_4(make_rsrc(Ln + bh * Nq + min(q, Nq), n), sls[buf], (uint32_t)lane * 4);
+      load_lds_4(make_rsrc(Dn + bh * Nq + min(q, Nq), n), sls[buf] + BT, (uint32_t)lane * 4);
     }
   };
 
@@ -407,8 +419,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       }
     }
     // first product for both 32-row halves, interleaved: S = Q K^T or dP = dO V^T; half j holds
-    // queries q0 + 32 j + 8 (r >> 2) + 4 h + (r & 3) of this key
-    f32x16 r2[2] = {f32x16{}, f32x16{}};
+    // queries q0 + 32 j + 8 (r >> 2) + 4 h + (r & 3) of this key.  The accumulators start at the
+    // rows' negated terms, so they end as S - LSE / scale (dV waves) or dP - D (dK waves).
+    f32x16 r2[2];
+    {
+      const float* rb = sc + (do_k ? BT : 0);
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 v4 = *(const f32x4*)(rb + 32 * half + 8 * g4 + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r2[half][4 * g4 + e] = v4[e];
+        }
+    }
+    u32x4 pw4[4];  // the dK waves' P of this block, from the pair's dV wave
+    if (do_k) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw4[i] = pw[64 * i];
+    }
     {
       const uint16_t* xa = do_k ? gc : qc;
 #pragma unroll
@@ -419,34 +448,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
     u32x4 pb[4];  // P (dV) or dS (dK) as the B operand of the second product, 16 queries each
     if (!do_k) {
-      // P = 2^(S scale log2e - reference), zero outside the causal / valid range, published for
-      // the pair's dK wave
+      // P = 2^((S - LSE / scale) scale log2e), zero outside the causal / valid range, published
+      // for the pair's dK wave (rows past Nq read a term of 0 and are masked)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int qh0 = q0 + 32 * half;
         const bool need = (qh0 + 32 > Nq) || (kw0 + 32 > Nk) || (CAUSAL && kw0 + 31 > qh0 + off);
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qi = 32 * half + 8 * g4 + 4 * h;  // first of this lane's four rows
-          const f32x4 l4 = *(const f32x4*)(sc + qi);
+        for (int r = 0; r < 16; r += 2) {
+          float p[2];
 #pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            const int r = 4 * g4 + e;
-            // (rows past Nq read a reference of 0 and are masked below)
-            float x0 = -l4[e], x1 = -l4[e + 1];
-            if constexpr (BIAS) {  // bias · log2e added to the exponent (bias / scale in scores)
-              x0 = fmaf(__uint_as_float(bq[16 * half + r] << 16), kLog2e, x0);
-              x1 = fmaf(__uint_as_float(bq[16 * half + r + 1] << 16), kLog2e, x1);
-            }
-            float p0 = fast_exp2(fmaf(r2[half][r], scale_log2, x0));
-            float p1 = fast_exp2(fmaf(r2[half][r + 1], scale_log2, x1));
-            if (need) {
-              const int q = q0 + qi + e;
-              if (!(q < Nq && my_k < Nk && (!CAUSAL || my_k <= q + off))) p0 = 0.f;
-              if (!(q + 1 < Nq && my_k < Nk && (!CAUSAL || my_k <= q + 1 + off))) p1 = 0.f;
-            }
-            const int j = 16 * half + r;
-            pb[j >> 3][(j >> 1) & 3] = pack_bf16x2(p0, p1);
+          for (int e = 0; e < 2; ++e) {
+            float x = r2[half][r + e] * scale_log2;
+            if constexpr (BIAS)  // bias · log2e added to the exponent (bias / scale in scores)
+              x = fmaf(__uint_as_float(bq[16 * half + r + e] << 16), kLog2e, x);
+            p[e] = fast_exp2(x);
+          }
+          const int j = 16 * half + r;
+          pb[j >> 3][(j >> 1) & 3] = pack_bf16x2(p[0], p[1]);
+        }
+        if (need) {  // clear the bf16 halves of masked entries
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const int q = qh0 + 8 * (r >> 2) + 4 * h + (r & 3), j = 16 * half + r;
+            const bool ok0 = q < Nq && my_k < Nk && (!CAUSAL || my_k <= q + off);
+            const bool ok1 = q + 1 < Nq && my_k < Nk && (!CAUSAL || my_k <= q + 1 + off);
+            pb[j >> 3][(j >> 1) & 3] &= (ok0 ? 0x0000ffffu : 0u) | (ok1 ? 0xffff0000u : 0u);
           }
         }
       }
@@ -454,22 +481,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       for (int i = 0; i < 4; ++i) pw[64 * i] = pb[i];
     } else {
       // dS = P (dP - D) from the pair's P of this block (zero wherever the pair is masked)
-      u32x4 pw4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pw4[i] = pw[64 * i];
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 d4 = *(const f32x4*)(sc + BT + 32 * half + 8 * g4 + 4 * h);
-#pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            const int r = 4 * g4 + e, j = 16 * half + r;
-            const uint32_t w = pw4[j >> 3][(j >> 1) & 3];
-            pb[j >> 3][(j >> 1) & 3] =
-                pack_bf16x2(__uint_as_float(w << 16) * (r2[half][r] - d4[e]),
-                            __uint_as_float(w & 0xffff0000u) * (r2[half][r + 1] - d4[e + 1]));
-          }
+        for (int r = 0; r < 16; r += 2) {
+          const int j = 16 * half + r;
+          const uint32_t w = pw4[j >> 3][(j >> 1) & 3];
+          pb[j >> 3][(j >> 1) & 3] = pack_bf16x2(__uint_as_float(w << 16) * r2[half][r],
+                                                 __uint_as_float(w & 0xffff0000u) * r2[half][r + 1]);
         }
     }
     // dK^T += Q^T dS or dV^T += dO^T P, 16 queries at a time, at raised priority so that the
@@ -494,7 +513,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
                   const void* bias, int bias_b, int bias_h, const AttnShape& s, float scale,
                   hipStream_t stream) {
   const long long rows = (long long)s.B * s.Hq * s.Nq;
-  float* const ws_l2 = ws_d + rows;  // the workspace holds D, then the log2-unit references
+  float* const ws_l2 = ws_d + rows;  // the workspace holds -D, then -LSE / scale
   const int nqt = (s.Nq + 127) / 128, nkt = (s.Nk + 127) / 128;
   constexpr int RPB = 256 / (D / 8);  // rows per prep workgroup
   const long long g_prep = (rows + RPB - 1) / RPB;
@@ -504,7 +523,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
   hipError_t e = hipSuccess;
   if (g_prep > 0) {
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)g_prep), dim3(256), 0, stream,
-                       (const uint16_t*)out, (const uint16_t*)dout, lse, ws_d, ws_l2, rows);
+                       (const uint16_t*)out, (const uint16_t*)dout, lse, ws_d, ws_l2, rows, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
