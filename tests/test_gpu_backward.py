@@ -149,6 +149,32 @@ def test_backward_deterministic_and_fully_written():
         assert np.array_equal(to_f64(a), b), f"{name} differs between two identical calls"
 
 
+def test_backward_workspace_holds_the_documented_row_terms():
+    # the workspace contract: fp32 -D [B, Hq, Nq], then -lse / scale [B, Hq, Nq] (-inf for rows
+    # whose lse is -inf); Nq > Nk causal gives such rows (the first Nq - Nk rows see no key)
+    B, Hq, Hkv, Nq, Nk, d = 1, 2, 2, 300, 130, 128
+    _, _, (q, k, v, out, lse, dout) = _run(B, Hq, Hkv, Nq, Nk, True, seed=4300)
+    s32 = _s32(d)
+    ws = torch.full((fa.attn_bwd_workspace_bytes(B, Hq, Nq),), 0x7f, dtype=torch.uint8,
+                    device="cuda")
+    fa.attn_bwd(q, k, v, out, lse, dout, causal=True, scale=s32, workspace=ws)
+    torch.cuda.synchronize()
+    rows = B * Hq * Nq
+    terms = ws.view(torch.float32).cpu().numpy().astype(np.float64)
+    dn, ln = terms[:rows], terms[rows:2 * rows]
+    o, g = to_f64(out).reshape(rows, d), to_f64(dout).reshape(rows, d)
+    dref = (o * g).sum(axis=1)
+    bound = 1e-6 * np.maximum(np.abs(o * g).sum(axis=1), 1e-30)
+    assert np.all(np.abs(dn + dref) <= bound), float(np.abs(dn + dref).max())
+    l32 = lse.cpu().numpy().reshape(rows)
+    dead = np.isneginf(l32)
+    assert dead.sum() == B * Hq * (Nq - Nk)
+    assert np.all(np.isneginf(ln[dead]))
+    lref = (-l32[~dead].astype(np.float32) / np.float32(s32)).astype(np.float64)
+    ulp = np.spacing(np.abs(lref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(ln[~dead] - lref) <= ulp)
+
+
 def test_backward_without_query_rows_zeroes_dk_dv():
     say("backward Nq=0")
     k = torch.ones((1, 2, 70, 128), dtype=torch.bfloat16, device="cuda")
