@@ -61,6 +61,7 @@ DECODE = ("decode_gqa_nq1", "decode_gqa_nq4")
 BRACKETS = 4
 KV_SETS = 4
 PROFILES = os.path.join(ROOT, "profiles")
+MFMA_BUSY_MAX = 0.9  # largest matrix-core busy fraction a clock reading may imply
 CSRC = os.path.join(ROOT, "scaled_dot_product_fa2_amd", "csrc")
 
 
@@ -542,10 +543,11 @@ def main():
 
     def checked_clock(clk, tflops):
         """A spin wave that shares a SIMD with busy, raised-priority waves can be issued late and
-        so overshoot its cycle count: a clock under which the measured rate would exceed the
-        matrix cores' peak at that clock is impossible and is withdrawn."""
+        so overshoot its cycle count, which reads as too low a clock.  The prefill kernel keeps
+        its matrix cores busy 0.58-0.68 of the cycles (SQ counters), so a reading under which the
+        measured rate would need them busy more than MFMA_BUSY_MAX of the cycles is withdrawn."""
         if clk.get("mhz") is not None and tflops is not None:
-            floor = tflops / PEAK_BF16_TFLOPS * 2400.0
+            floor = tflops / (PEAK_BF16_TFLOPS * MFMA_BUSY_MAX) * 2400.0
             if clk["mhz"] < floor:
                 return {**clk, "mhz": None, "mhz_read": clk["mhz"],
                         "note": f"spin starved: the measured rate needs at least {floor:.0f} MHz"}
