@@ -455,6 +455,19 @@ def roofline_hbm(nbytes, ms, traffic):
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic}
 
 
+def checked_clock(clk, tflops):
+    """A spin wave that shares a SIMD with busy, raised-priority waves can be issued late and so
+    overshoot its cycle count, which reads as too low a clock.  The prefill kernel keeps its
+    matrix cores busy 0.58-0.68 of the cycles (SQ counters), so a reading under which the measured
+    rate would need them busy more than MFMA_BUSY_MAX of the cycles is withdrawn."""
+    if clk.get("mhz") is not None and tflops is not None:
+        floor = tflops / (PEAK_BF16_TFLOPS * MFMA_BUSY_MAX) * 2400.0
+        if clk["mhz"] < floor:
+            return {**clk, "mhz": None, "mhz_read": clk["mhz"],
+                    "note": f"spin starved: the measured rate needs at least {floor:.0f} MHz"}
+    return clk
+
+
 def device_record(torch):
     p = torch.cuda.get_device_properties(0)
     rocm = None
@@ -540,18 +553,6 @@ def main():
 
     def r5(x):
         return round(x, 5)
-
-    def checked_clock(clk, tflops):
-        """A spin wave that shares a SIMD with busy, raised-priority waves can be issued late and
-        so overshoot its cycle count, which reads as too low a clock.  The prefill kernel keeps
-        its matrix cores busy 0.58-0.68 of the cycles (SQ counters), so a reading under which the
-        measured rate would need them busy more than MFMA_BUSY_MAX of the cycles is withdrawn."""
-        if clk.get("mhz") is not None and tflops is not None:
-            floor = tflops / (PEAK_BF16_TFLOPS * MFMA_BUSY_MAX) * 2400.0
-            if clk["mhz"] < floor:
-                return {**clk, "mhz": None, "mhz_read": clk["mhz"],
-                        "note": f"spin starved: the measured rate needs at least {floor:.0f} MHz"}
-        return clk
 
     def prefill_obj(name):
         w, t = W[name], st[name]
