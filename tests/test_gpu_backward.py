@@ -8,7 +8,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from gpu_helpers import say, to_f64, upload  # noqa: E402
+from gpu_helpers import BF16_MAX_ABS, BF16_MEAN_ABS, compare, say, to_f64, upload  # noqa: E402
 from oracle import attention as A  # noqa: E402
 from scaled_dot_product_fa2_amd import binding as fa  # noqa: E402
 from scaled_dot_product_fa2_amd import inputs as I  # noqa: E402
@@ -147,6 +147,29 @@ def test_backward_deterministic_and_fully_written():
     for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), got):
         assert not bool(torch.isnan(a.float()).any()), f"{name} not fully written"
         assert np.array_equal(to_f64(a), b), f"{name} differs between two identical calls"
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -32, 2.0 ** -10, 0.5, 2.0])
+def test_backward_at_other_scales(scale):
+    # the row terms -LSE / scale and the exponent argument (S - LSE / scale) * scale * log2e at
+    # scales from the accepted floor (near-uniform softmax) to sharply peaked rows
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 200, 260, 128
+    x = I.draw_qkv(4400, B, Hq, Hkv, Nq, Nk, d)
+    g_bits = I.draw_grad(4401, (B, Hq, Nq, d))
+    q, k, v = upload(x)
+    dout = I.to_device(g_bits, "bf16")
+    s32 = float(np.float32(scale))
+    say(f"backward at scale {s32!r}")
+    out, lse = fa.attn_fwd(q, k, v, causal=True, scale=s32)
+    dq, dk, dv = fa.attn_bwd(q, k, v, out, lse, dout, causal=True, scale=s32)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = A.attention_fp64(*x.as_f64(), s32, True)
+    compare(to_f64(out), to_f64(lse), O_ref, lse_ref, BF16_MAX_ABS, BF16_MEAN_ABS,
+            what=f"forward at scale {s32!r}")
+    g = I.bf16_bits_to_f32(g_bits).astype(np.float64)
+    rq, rk, rv = A.attention_backward_fp64(*x.as_f64(), g, s32, True)
+    for name, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), (rq, rk, rv)):
+        _check(name, to_f64(a), r)
 
 
 def test_backward_workspace_holds_the_documented_row_terms():
