@@ -17,7 +17,7 @@
 //     dS are per-lane formulas with the row's LSE and D; dQ^T += K^T dS^T takes K^T from the
 //     transposing LDS read and dS^T straight from the registers.
 //   * bwd_dkdv_kernel: the transpose of that.  A workgroup owns 128 keys (32 per wave pair);
-//     64-row blocks of Q and dO (and their LSE, D) stream through LDS, over every query head that
+//     64-row blocks of Q and dO (and their row terms) stream through LDS, over every query head that
 //     shares the K/V head.  S = Q K^T and dP = dO V^T put one key per lane; eight waves share each
 //     block: four compute S, P and dV^T += dO^T P, four dP and, with P passed through LDS one step
 //     later, dS and dK^T += Q^T dS, so each wave runs two products and holds one accumulator set
