@@ -8,11 +8,12 @@
 // (D_i equals sum_k P_ik dP_ik, the softmax Jacobian's centring term, because O = P V).  Key and
 // value heads shared by several query heads receive the sum over those heads.
 //
-// gfx950 mapping, three launches on one stream:
-//   * bwd_prep_kernel: per query row -D and -LSE / scale (the row terms), which start the
-//     accumulators of the score products so that they end as dP - D and S - LSE / scale.
+// gfx950 mapping, two launches on one stream:
 //   * bwd_dq_kernel: the forward's structure.  A workgroup owns 128 query rows (32 per wave, Q
 //     and dO held in registers as the B operand); 64-key blocks of K and V stream HBM -> LDS.
+//     It also computes each row's D from O and dO and writes the row terms -D and -LSE / scale
+//     to the workspace; they start the dK/dV kernel's score accumulators, which therefore end as
+//     dP - D and S - LSE / scale.
 //     S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 put one query per lane, so P and
 //     dS are per-lane formulas with the row's LSE and D; dQ^T += K^T dS^T takes K^T from the
 //     transposing LDS read and dS^T straight from the registers.
@@ -129,39 +130,6 @@ __device__ __forceinline__ void store_rowT(uint16_t* row_ptr, const f32x16 (&acc
     }
 }
 
-// Per query row, negated so that they can start the accumulators of the score products:
-// Dn[row] = -sum_d dO[row][d] * O[row][d] (D/8 lanes per row, 8 dims each), and
-// Ln[row] = -LSE[row] / scale, the row's reference in score units, or -inf for a row with no
-// visible key (LSE = -inf) so that every P of it is exactly 0.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O,
-                                                       const uint16_t* __restrict__ dO,
-                                                       const float* __restrict__ LSE,
-                                                       float* __restrict__ Dn,
-                                                       float* __restrict__ Ln, long long rows,
-                                                       float scale) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR;  // lanes per row, rows per workgroup
-  const long long row = (long long)blockIdx.x * RPB + (threadIdx.x / LPR);
-  const int sub = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 o = *(const u32x4*)(O + row * D + 8 * sub);
-    const u32x4 g = *(const u32x4*)(dO + row * D + 8 * sub);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc += __uint_as_float(o[i] << 16) * __uint_as_float(g[i] << 16);
-      acc += __uint_as_float(o[i] & 0xffff0000u) * __uint_as_float(g[i] & 0xffff0000u);
-    }
-  }
-#pragma unroll
-  for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-  if (row < rows && sub == 0) {
-    Dn[row] = -acc;
-    const float l = LSE[row];
-    Ln[row] = l == -INFINITY ? -INFINITY : -l / scale;
-  }
-}
-
 // The per-lane P and dS of one C tile from its scores s and dP values (both in place: s -> P,
 // dp -> dS), given the reference (LSE in log2 units) and D of each element.
 __device__ __forceinline__ void p_and_ds(float& s, float& dp, float c, float lse2, float dd) {
@@ -176,7 +144,8 @@ template <int D, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ Ln, const float* __restrict__ Dn, uint16_t* __restrict__ dQ,
+    const uint16_t* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ Ln,
+    float* __restrict__ Dn, uint16_t* __restrict__ dQ,
     const int* __restrict__ seqlens, const uint16_t* __restrict__ bias, int bias_b, int bias_h,
     int Hq, int Hkv, int Nq, int Nk_cap, int nqt, float scale, float scale_log2) {
   constexpr int TILE = Geo<D>::TILE, NCB = Geo<D>::NCB, NDB = Geo<D>::NDB;
@@ -212,23 +181,44 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       BIAS ? (uint32_t)max(0, min(32, Nq - qw0)) * Nk_cap * 2 : 0u);
   const uint32_t b_lane = (uint32_t)l32 * Nk_cap * 2 + 8u * h;
 
-  // Q and dO of this lane's query as the B operand (dims 16c + 8h .. +7)
+  // Q and dO of this lane's query as the B operand (dims 16c + 8h .. +7), and O's same dims for
+  // D = sum_d dO O: the lane's 8-dim dot products summed as a tree, then the partner lane's half
   u32x4 qf[NCB], gf[NCB];
+  float dd;
   {
     const bool ok = my_q < Nq;
-    const uint16_t* qrow = Q + ((size_t)bh * Nq + min(my_q, Nq - 1)) * D;
-    const uint16_t* grow = dO + ((size_t)bh * Nq + min(my_q, Nq - 1)) * D;
+    const size_t row = (size_t)bh * Nq + min(my_q, Nq - 1);
+    float part[NCB];
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
-      qf[c] = ok ? *(const u32x4*)(qrow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
-      gf[c] = ok ? *(const u32x4*)(grow + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+      qf[c] = ok ? *(const u32x4*)(Q + row * D + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+      gf[c] = ok ? *(const u32x4*)(dO + row * D + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 o = ok ? *(const u32x4*)(O + row * D + 16 * c + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a += __uint_as_float(o[i] << 16) * __uint_as_float(gf[c][i] << 16);
+        a += __uint_as_float(o[i] & 0xffff0000u) * __uint_as_float(gf[c][i] & 0xffff0000u);
+      }
+      part[c] = a;
     }
+#pragma unroll
+    for (int w = 1; w < NCB; w *= 2)
+#pragma unroll
+      for (int c = 0; c + w < NCB; c += 2 * w) part[c] += part[c + w];
+    dd = part[0] + __shfl_xor(part[0], 32);
   }
-  // the row's reference in log2 units, LSE log2e (+inf: no visible key, so every P is 0), and D
-  float lse2 = INFINITY, dd = 0.f;
+  // the row's reference in log2 units, LSE log2e (+inf: no visible key, so every P is 0); the
+  // row terms -D and -LSE / scale (-inf for such a row) go to the workspace for the dK/dV kernel
+  float lse2 = INFINITY;
   if (my_q < Nq) {
-    lse2 = -Ln[(size_t)bh * Nq + my_q] * scale_log2;
-    dd = -Dn[(size_t)bh * Nq + my_q];
+    const size_t row = (size_t)bh * Nq + my_q;
+    const float l = LSE[row];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    if (h == 0) {
+      Dn[row] = -dd;
+      Ln[row] = l == -INFINITY ? -INFINITY : -l / scale;
+    }
   }
 
   const TileLanes tl = tile_lanes<D>(lane);
@@ -515,15 +505,16 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
   const long long rows = (long long)s.B * s.Hq * s.Nq;
   float* const ws_l2 = ws_d + rows;  // the workspace holds -D, then -LSE / scale
   const int nqt = (s.Nq + 127) / 128, nkt = (s.Nk + 127) / 128;
-  constexpr int RPB = 256 / (D / 8);  // rows per prep workgroup
-  const long long g_prep = (rows + RPB - 1) / RPB;
   const long long g_dq = (long long)s.B * s.Hq * nqt, g_kv = (long long)s.B * s.Hkv * nkt;
-  if (g_prep > 0x7fffffffLL || g_dq > 0x7fffffffLL || g_kv > 0x7fffffffLL)
-    return hipErrorInvalidConfiguration;
+  if (g_dq > 0x7fffffffLL || g_kv > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipError_t e = hipSuccess;
-  if (g_prep > 0) {
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)g_prep), dim3(256), 0, stream,
-                       (const uint16_t*)out, (const uint16_t*)dout, lse, ws_d, ws_l2, rows, scale);
+  // the dQ kernel first: it also writes the row terms the dK/dV kernel reads
+  if (g_dq > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, BIAS>), dim3((unsigned)g_dq), dim3(256), 0,
+                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                       (const uint16_t*)dout, (const uint16_t*)out, lse, ws_l2, ws_d,
+                       (uint16_t*)dq, seqlens, (const uint16_t*)bias, bias_b, bias_h, s.Hq, s.Hkv,
+                       s.Nq, s.Nk, nqt, scale, scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -533,15 +524,6 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* out, 
                        (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dk,
                        (uint16_t*)dv, seqlens, (const uint16_t*)bias, bias_b, bias_h, s.Hq, s.Hkv,
                        s.Nq, s.Nk, nkt, scale, scale * kLog2e);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (g_dq > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, BIAS>), dim3((unsigned)g_dq), dim3(256), 0,
-                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dout, (const float*)ws_l2, (const float*)ws_d, (uint16_t*)dq,
-                       seqlens, (const uint16_t*)bias, bias_b, bias_h, s.Hq, s.Hkv, s.Nq, s.Nk, nqt,
-                       scale, scale * kLog2e);
     e = hipGetLastError();
   }
   return e;
