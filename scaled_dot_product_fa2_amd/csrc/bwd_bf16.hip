@@ -276,13 +276,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
         p_and_ds(s0, d0, scale_log2, l0, dd);
         p_and_ds(s1, d1, scale_log2, l1, dd);
-        if (need) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > lim) d0 = 0.f;
-          if (key + 1 > lim) d1 = 0.f;
-        }
         const int j = 16 * kb + r;
         pb[j >> 3][(j >> 1) & 3] = pack_bf16x2(d0, d1);
+      }
+      if (need) {  // clear the bf16 halves of dS entries past the last visible key
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3), j = 16 * kb + r;
+          pb[j >> 3][(j >> 1) & 3] &= (key <= lim ? 0x0000ffffu : 0u) | (key + 1 <= lim ? 0xffff0000u : 0u);
+        }
       }
     }
     // dQ^T += K^T dS^T, 16 keys at a time
