@@ -262,9 +262,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       f32x16 s = f32x16{}, dp = f32x16{};
       // the operands of slice c are read PF slices ahead of their products into a ring, and the
       // scheduling fences keep that distance: left to itself the compiler reads each operand
-      // right before its product and waits for it there (the bias variant, short of registers,
-      // keeps that order)
-      constexpr int PF = BIAS ? 0 : 3, NR = PF + 1;
+      // right before its product and waits for it there
+      constexpr int PF = 3, NR = PF + 1;
       u32x4 ak[NR], av[NR];
 #pragma unroll
       for (int c = 0; c < PF; ++c) {
@@ -279,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
         s = mfma32x32x16(ak[c % NR], qf[c], s);
         dp = mfma32x32x16(av[c % NR], gf[c], dp);
-        if constexpr (PF > 0) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
@@ -447,9 +446,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       for (int i = 0; i < 4; ++i) pw4[i] = pw[64 * i];
     }
     {
-      // operands read PF slices ahead into a ring, as in the dQ kernel (not in the bias variant)
+      // operands read PF slices ahead into a ring, as in the dQ kernel
       const uint16_t* xa = do_k ? gc : qc;
-      constexpr int PF = BIAS ? 0 : 2, NR = PF + 1;
+      constexpr int PF = 2, NR = PF + 1;
       u32x4 ar[NR][2];
 #pragma unroll
       for (int c = 0; c < PF; ++c)
@@ -465,7 +464,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int half = 0; half < 2; ++half)
           r2[half] = mfma32x32x16(ar[c % NR][half], bf[c], r2[half]);
-        if constexpr (PF > 0) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     u32x4 pb[4];  // P (dV) or dS (dK) as the B operand of the second product, 16 queries each
