@@ -26,6 +26,8 @@
 //   The LDS tiles use one XOR swizzle, chunk c of row r at c ^ ((r & 3) << 2 | (r >> 2) & 3),
 //   under which both access patterns are conflict-free: 16 consecutive rows at one chunk (the
 //   row-wise operand reads) and 4 consecutive rows x 4 chunks (the transposing reads).
+//   In both kernels the first products' operands are read from LDS a few slices ahead into a
+//   register ring, fenced so that the compiler keeps the distance.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
