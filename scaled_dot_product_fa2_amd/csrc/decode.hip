@@ -210,7 +210,8 @@ __global__ __launch_bounds__(64 * NW, NW == 1 ? 1 : 2) void decode_split_kernel(
   // costs depends on where the K/V allocations fall (GQA decode at Nq = 4: 47.8 -> 46.9 us,
   // and 51.7 -> 48.8 us with other allocations made first).  The order changes only the
   // summation order of the split's partial.
-  const int rot = nkb > 0 ? (s * 7 + (b * Hkv + hkv) * 5) % nkb : 0;
+  const int rot =
+      nkb > 0 ? (int)((7u * (unsigned)s + 5u * (unsigned)(b * Hkv + hkv)) % (unsigned)nkb) : 0;
   auto phys = [&](int j) { const int k = j + rot; return k >= nkb ? k - nkb : k; };
 #pragma unroll
   for (int u = 0; u < NB; ++u)
